@@ -1,0 +1,152 @@
+"""fp64 reference attention (forward and backward), row-blocked.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Readings taken where the pages are silent (each is listed in the design
+notes with its reason):
+
+* scale defaults to 1/sqrt(d) -- the d_k of the attention equation in
+  "FlashAttention — フラッシュアテンション" (標準的なアテンションの問題点);
+* causal: key j is visible to query i iff j <= i (diagonal included);
+* GQA: query head h reads K/V head floor(h / (H / H_kv)) (contiguous groups);
+* LSE_i = ln sum_{j visible} exp(S_ij), natural log, scale included -- the
+  softmax normalisation statistic that "FlashAttentionとは？…" (section
+  逆伝播でL×L行列を保存せず再計算する設計) says the forward keeps for the
+  backward;
+* the backward is the textbook chain rule through the row softmax (the pages
+  give only "recompute P from Q/K blocks with the saved statistics").
+
+Inputs are float64 numpy arrays holding exactly the values a kernel receives
+(bf16-rounded or fp8-dequantised upstream).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 512
+
+
+def kv_head_of(h: int, H: int, H_kv: int) -> int:
+    """Grouped-query head map: H/H_kv consecutive query heads share a K/V head.
+
+    GQA support is listed under FlashAttention-2 in "FlashAttention — フラッシュ
+    アテンション" (進化と関連技術); the contiguous grouping is the reading taken.
+    """
+    if H % H_kv:
+        raise ValueError("H must be a multiple of H_kv")
+    return h // (H // H_kv)
+
+
+def scores_rows(q_rows, k, scale, causal, row_ids):
+    """S = scale * Q K^T for the given query rows, masked entries set to -inf.
+
+    The attention equation's argument QK^T/sqrt(d_k) ("FlashAttention —
+    フラッシュアテンション", 標準的なアテンションの問題点), with the causal mask
+    of the FA2 paragraph of "Flash Attention 2 / 3 とは 2026年版" (FA2 の改善):
+    query i sees keys 0..i.
+    """
+    s = scale * (q_rows @ k.T)
+    if causal:
+        n_k = k.shape[0]
+        cols = np.arange(n_k)[None, :]
+        rows = np.asarray(row_ids)[:, None]
+        s = np.where(cols <= rows, s, -np.inf)
+    return s
+
+
+def softmax_rows(s):
+    """Row softmax P = exp(S - m) / sum exp(S - m) and its logsumexp m + ln l.
+
+    Subtracting the row max does not change P (it cancels in the ratio); it is
+    the max that the online softmax of "FlashAttentionとは？…" (最大値と正規化項を
+    持ち回るオンラインsoftmaxの再スケール) carries, here taken over the whole row
+    at once.
+    """
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=1, keepdims=True)
+    p = e / l
+    lse = (m + np.log(l))[:, 0]
+    return p, lse
+
+
+def forward_rows(q, k, v, scale, causal, rows):
+    """O and LSE for selected query rows of one head (q [N,d], k/v [N_k,d])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    for r0 in range(0, rows.size, ROW_BLOCK):
+        rid = rows[r0:r0 + ROW_BLOCK]
+        s = scores_rows(q[rid], k, scale, causal, rid)
+        p, lse[r0:r0 + ROW_BLOCK] = softmax_rows(s)
+        o[r0:r0 + ROW_BLOCK] = p @ v
+    return o, lse
+
+
+def forward_head(q, k, v, scale, causal):
+    """Attention(Q,K,V) = softmax(QK^T * scale) V for every row of one head."""
+    return forward_rows(q, k, v, scale, causal, np.arange(q.shape[0]))
+
+
+def forward(q, k, v, scale=None, causal=True):
+    """All heads: q [B,H,N,d], k/v [B,H_kv,N,d] -> O [B,H,N,d], LSE [B,H,N]."""
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, kv], v[b, kv], scale, causal)
+    return o, lse
+
+
+def backward_head(q, k, v, do, scale, causal):
+    """Gradients of L = sum(O * dO) with respect to Q, K, V for one head.
+
+    Recomputes P from Q and K (the backward-by-recompute paragraph of
+    "FlashAttentionとは？…", 逆伝播でL×L行列を保存せず再計算する設計) and applies
+    the chain rule of O = P V and of the row softmax:
+      dV = P^T dO;  dP = dO V^T;  dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik);
+      dQ = scale dS K;  dK = scale dS^T Q.
+    Returns dq, dk, dv, O, LSE (all float64).
+    """
+    n_q, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.empty((n_q, v.shape[1]))
+    lse = np.empty(n_q)
+    for r0 in range(0, n_q, ROW_BLOCK):
+        rid = np.arange(r0, min(n_q, r0 + ROW_BLOCK))
+        s = scores_rows(q[rid], k, scale, causal, rid)
+        p, lse[rid] = softmax_rows(s)
+        o[rid] = p @ v
+        dp = do[rid] @ v.T
+        row_dot = np.sum(p * dp, axis=1, keepdims=True)
+        ds = p * (dp - row_dot)
+        dq[rid] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[rid])
+        dv += p.T @ do[rid]
+    return dq, dk, dv, o, lse
+
+
+def backward(q, k, v, do, scale=None, causal=True):
+    """All heads; K/V gradients of a GQA group are summed over its query heads."""
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            gq, gk, gv, _, _ = backward_head(q[b, h], k[b, kv], v[b, kv], do[b, h], scale, causal)
+            dq[b, h] = gq
+            dk[b, kv] += gk
+            dv[b, kv] += gv
+    return dq, dk, dv

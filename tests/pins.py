@@ -1,0 +1,235 @@
+"""Checks that tie the oracle to facts outside itself.
+
+Each ``pin_*`` takes an implementation namespace ``impl`` exposing
+``forward(q,k,v,scale,causal)``, ``forward_rows(q,k,v,scale,causal,rows)``,
+``softmax_rows(s)``, ``scores_rows(...)`` and ``backward(q,k,v,do,scale,causal)``
+(the oracle, or a deliberately broken copy of it in the mutation test) and
+raises AssertionError when the implementation disagrees with:
+
+* closed forms the definition fixes (identical keys, a dominant key, row 0
+  under the causal mask, a hand-worked two-token example);
+* invariants (row sums of P, permutation of K/V rows, shifts of K and V);
+* an independent scalar brute force written here with ``math.exp``/``math.fsum``;
+* central finite differences of L = sum(O * dO) for the gradients;
+* gradient identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- forward ---
+
+def pin_rows_sum_to_one(impl):
+    rng = _rng(11)
+    for causal in (False, True):
+        q, k = rng.standard_normal((9, 5)), rng.standard_normal((9, 5))
+        s = impl.scores_rows(q, k, 0.7, causal, np.arange(9))
+        p, _ = impl.softmax_rows(s)
+        assert np.all(p >= 0)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-14
+        if causal:
+            assert np.all(p[np.triu_indices(9, 1)] == 0.0)
+
+
+def pin_identical_keys(impl):
+    """All keys equal: P is uniform over visible keys, O is the (prefix) mean of V."""
+    rng = _rng(12)
+    N, d = 13, 6
+    q = rng.standard_normal((1, 1, N, d))
+    k = np.repeat(rng.standard_normal((1, 1, 1, d)), N, axis=2)
+    v = rng.standard_normal((1, 1, N, d))
+    scale = 0.37
+    for causal in (False, True):
+        o, lse = impl.forward(q, k, v, scale, causal)
+        qk = scale * (q[0, 0] @ k[0, 0, 0])
+        for i in range(N):
+            n_vis = i + 1 if causal else N
+            want = v[0, 0, :n_vis].mean(axis=0)
+            assert np.max(np.abs(o[0, 0, i] - want)) < 1e-13
+            assert abs(lse[0, 0, i] - (qk[i] + math.log(n_vis))) < 1e-12
+
+
+def pin_dominant_key(impl):
+    """K_j = c e_j, Q_i = e_pi(i), scale 1: row i puts weight ~1 on key pi(i)."""
+    N = d = 8
+    c = 50.0
+    k = c * np.eye(N)[None, None]
+    v = _rng(13).standard_normal((1, 1, N, d))
+    for causal in (False, True):
+        pi = [i // 2 for i in range(N)] if causal else [(3 * i + 1) % N for i in range(N)]
+        q = np.eye(N)[pi][None, None]
+        o, lse = impl.forward(q, k, v, 1.0, causal)
+        for i in range(N):
+            assert np.max(np.abs(o[0, 0, i] - v[0, 0, pi[i]])) < 1e-15
+            n_vis = i + 1 if causal else N
+            want_lse = c + math.log1p((n_vis - 1) * math.exp(-c))
+            assert abs(lse[0, 0, i] - want_lse) < 1e-12
+
+
+def pin_causal_row0(impl):
+    rng = _rng(14)
+    q, k, v = (rng.standard_normal((2, 3, 7, 4)) for _ in range(3))
+    o, lse = impl.forward(q, k, v, 0.5, True)
+    assert np.max(np.abs(o[:, :, 0] - v[:, :, 0])) < 1e-15
+    want = 0.5 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0] - want)) < 1e-14
+
+
+def pin_permutation_invariance(impl):
+    rng = _rng(15)
+    q, k, v = (rng.standard_normal((1, 2, 11, 5)) for _ in range(3))
+    perm = rng.permutation(11)
+    o1, l1 = impl.forward(q, k, v, 0.8, False)
+    o2, l2 = impl.forward(q, k[:, :, perm], v[:, :, perm], 0.8, False)
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.max(np.abs(l1 - l2)) < 1e-13
+
+
+def pin_shifts(impl):
+    rng = _rng(16)
+    q, k, v = (rng.standard_normal((1, 1, 10, 4)) for _ in range(3))
+    c = rng.standard_normal(4)
+    for causal in (False, True):
+        o, lse = impl.forward(q, k, v, 0.6, causal)
+        o_k, lse_k = impl.forward(q, k + c, v, 0.6, causal)      # K -> K + 1 c^T
+        assert np.max(np.abs(o_k - o)) < 1e-12
+        assert np.max(np.abs(lse_k - (lse + 0.6 * (q[..., :] @ c)))) < 1e-12
+        o_v, lse_v = impl.forward(q, k, v + c, 0.6, causal)      # V -> V + 1 c^T
+        assert np.max(np.abs(o_v - (o + c))) < 1e-12 and np.max(np.abs(lse_v - lse)) < 1e-15
+        o_a, lse_a = impl.forward(2.5 * q, k, v, 0.6 / 2.5, causal)  # (aQ, s/a) == (Q, s)
+        assert np.max(np.abs(o_a - o)) < 1e-12 and np.max(np.abs(lse_a - lse)) < 1e-12
+
+
+def brute_force_forward(q, k, v, scale, causal, H_kv):
+    """Scalar loops with math.exp and math.fsum; no numpy arithmetic."""
+    B, H, N, d = q.shape
+    g = H // H_kv
+    o = [[[[0.0] * v.shape[3] for _ in range(N)] for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * N for _ in range(H)] for _ in range(B)]
+    for b, h, i in itertools.product(range(B), range(H), range(N)):
+        kv = h // g
+        js = range(i + 1) if causal else range(N)
+        s = {j: scale * math.fsum(float(q[b, h, i, t]) * float(k[b, kv, j, t]) for t in range(d))
+             for j in js}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in js}
+        tot = math.fsum(w.values())
+        lse[b][h][i] = mx + math.log(tot)
+        for t in range(v.shape[3]):
+            o[b][h][i][t] = math.fsum(w[j] * float(v[b, kv, j, t]) for j in js) / tot
+    return np.array(o), np.array(lse)
+
+
+def pin_brute_force(impl):
+    rng = _rng(17)
+    cases = [(1, 1, 1, 1, 1), (1, 2, 2, 5, 3), (2, 4, 2, 9, 4), (1, 4, 1, 16, 8), (1, 3, 3, 16, 2)]
+    for (B, H, H_kv, N, d), causal in itertools.product(cases, (False, True)):
+        q = rng.standard_normal((B, H, N, d)) * 1.5
+        k = rng.standard_normal((B, H_kv, N, d)) * 1.5
+        v = rng.standard_normal((B, H_kv, N, d))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = impl.forward(q, k, v, scale, causal)
+        o_b, lse_b = brute_force_forward(q, k, v, scale, causal, H_kv)
+        assert np.max(np.abs(o - o_b)) < 1e-13, (B, H, H_kv, N, d, causal)
+        assert np.max(np.abs(lse - lse_b)) < 1e-13
+
+
+def pin_worked_example(impl):
+    """Two tokens, d = 1, scale 1: q = (1, 2), k = (0, 1), v = (1, 3).
+
+    Row 0 scores (0, 1), row 1 scores (0, 2), so with e = exp(1):
+      non-causal O = ((1+3e)/(1+e), (1+3e^2)/(1+e^2)), LSE = (ln(1+e), ln(1+e^2));
+      causal     O = (1, (1+3e^2)/(1+e^2)),          LSE = (0, ln(1+e^2)).
+    """
+    e = math.e
+    q = np.array([1.0, 2.0]).reshape(1, 1, 2, 1)
+    k = np.array([0.0, 1.0]).reshape(1, 1, 2, 1)
+    v = np.array([1.0, 3.0]).reshape(1, 1, 2, 1)
+    want = {
+        False: ([(1 + 3 * e) / (1 + e), (1 + 3 * e * e) / (1 + e * e)],
+                [math.log(1 + e), math.log(1 + e * e)]),
+        True: ([1.0, (1 + 3 * e * e) / (1 + e * e)], [0.0, math.log(1 + e * e)]),
+    }
+    for causal, (wo, wl) in want.items():
+        o, lse = impl.forward(q, k, v, 1.0, causal)
+        assert np.max(np.abs(o.reshape(2) - wo)) < 1e-15
+        assert np.max(np.abs(lse.reshape(2) - wl)) < 1e-15
+
+
+def pin_forward_rows(impl):
+    """Row subsets give the same rows as the full computation."""
+    rng = _rng(18)
+    q, k, v = (rng.standard_normal((40, 6)) for _ in range(3))
+    rows = [0, 3, 17, 39]
+    for causal in (False, True):
+        of, lf = impl.forward(q[None, None], k[None, None], v[None, None], 0.4, causal)
+        orow, lrow = impl.forward_rows(q, k, v, 0.4, causal, rows)
+        assert np.max(np.abs(orow - of[0, 0, rows])) < 1e-14
+        assert np.max(np.abs(lrow - lf[0, 0, rows])) < 1e-14
+
+
+# --------------------------------------------------------------- backward ---
+
+def _loss(impl, q, k, v, do, scale, causal):
+    o, _ = impl.forward(q, k, v, scale, causal)
+    return math.fsum((o * do).ravel().tolist())
+
+
+def pin_finite_differences(impl):
+    rng = _rng(19)
+    h = 1e-6
+    for (B, H, H_kv, N, d), causal in itertools.product([(1, 1, 1, 6, 3), (1, 4, 2, 5, 2)], (False, True)):
+        q = rng.standard_normal((B, H, N, d))
+        k = rng.standard_normal((B, H_kv, N, d))
+        v = rng.standard_normal((B, H_kv, N, d))
+        do = rng.standard_normal((B, H, N, d))
+        scale = 0.9
+        dq, dk, dv = impl.backward(q, k, v, do, scale, causal)
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy(); xp[idx] += h
+                xm = x.copy(); xm[idx] -= h
+                args = {"q": q, "k": k, "v": v}
+                lp = _loss(impl, *(xp if n == name else args[n] for n in "qkv"), do, scale, causal)
+                lm = _loss(impl, *(xm if n == name else args[n] for n in "qkv"), do, scale, causal)
+                num[idx] = (lp - lm) / (2 * h)
+            assert np.max(np.abs(num - g)) < 1e-7, (name, causal, np.max(np.abs(num - g)))
+
+
+def pin_gradient_identities(impl):
+    rng = _rng(20)
+    B, H, H_kv, N, d = 2, 4, 2, 12, 5
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H_kv, N, d))
+    v = rng.standard_normal((B, H_kv, N, d))
+    do = rng.standard_normal((B, H, N, d))
+    for causal in (False, True):
+        dq, dk, dv = impl.backward(q, k, v, do, 0.45, causal)
+        assert np.max(np.abs(dk.sum(axis=2))) < 1e-12                       # sum_j dS_ij = 0
+        do_group = do.reshape(B, H_kv, H // H_kv, N, d).sum(axis=2)
+        assert np.max(np.abs(dv.sum(axis=2) - do_group.sum(axis=2))) < 1e-12  # P rows sum to 1
+        if causal:
+            # the last key is seen only by the last query: dV_{N-1} = sum over group of dO_{N-1} * P[N-1,N-1]
+            _, lse = impl.forward(q, k, v, 0.45, True)
+            g = H // H_kv
+            for b, kv in itertools.product(range(B), range(H_kv)):
+                want = np.zeros(d)
+                for h in range(kv * g, (kv + 1) * g):
+                    p_last = math.exp(0.45 * float(q[b, h, N - 1] @ k[b, kv, N - 1]) - lse[b, h, N - 1])
+                    want += p_last * do[b, h, N - 1]
+                assert np.max(np.abs(dv[b, kv, N - 1] - want)) < 1e-12
+
+
+FORWARD_PINS = [pin_rows_sum_to_one, pin_identical_keys, pin_dominant_key, pin_causal_row0,
+                pin_permutation_invariance, pin_shifts, pin_brute_force, pin_worked_example,
+                pin_forward_rows]
+BACKWARD_PINS = [pin_finite_differences, pin_gradient_identities]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -1,0 +1,125 @@
+"""CPU tests that pin the fp64 oracle to facts outside itself.
+
+Besides the pins of ``tests/pins.py`` this file cross-checks the oracle with
+PyTorch's own CPU attention (a library routine computing the same
+definition), compares it with the fp32 rounding level the pages measured for
+two exact CPU implementations, and plants mistakes in copies of the oracle to
+show that every plausible slip is caught by at least one pin.
+"""
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import oracle.attention as oa
+from tests import pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oa)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 33, 16), (1, 8, 2, 70, 32), (1, 2, 1, 129, 64)])
+def test_matches_torch_sdpa_fp64(shape, causal):
+    """Library cross-check: torch's CPU SDPA (math path) in float64, with autograd."""
+    B, H, H_kv, N, d = shape
+    g = torch.Generator().manual_seed(sum(shape) + causal)
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    do = torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    rep = H // H_kv
+    ref = F.scaled_dot_product_attention(q, k.repeat_interleave(rep, 1), v.repeat_interleave(rep, 1),
+                                         is_causal=causal)
+    ref.backward(do)
+    o, lse = oracle.forward(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(), None, causal)
+    assert np.max(np.abs(o - ref.detach().numpy())) < 1e-12
+    # logsumexp cross-check against torch.logsumexp of the masked scores
+    s = (q @ k.repeat_interleave(rep, 1).transpose(-1, -2)).detach() / math.sqrt(d)
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    assert np.max(np.abs(lse - torch.logsumexp(s, -1).numpy())) < 1e-12
+    dq, dk, dv = oracle.backward(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                                 do.numpy(), None, causal)
+    assert np.max(np.abs(dq - q.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dk - k.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dv - v.grad.numpy())) < 1e-11
+
+
+def _page_fp32_errors():
+    path = os.path.join(os.path.dirname(__file__), "golden", "cpu_sdpa_fp32_error.txt")
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                n, e = line.split()
+                out[int(n)] = float(e)
+    return out
+
+
+def test_fp32_rounding_level_matches_pages():
+    """torch's fused CPU fp32 attention lands within the pages' fp32 error level of the oracle.
+
+    The pages measured ~1e-6 between two exact fp32 CPU paths at B=1, H=8,
+    N=1024, d=64, causal.  An fp32 fused implementation must sit at that level
+    against the fp64 oracle; an oracle with a wrong term would be far off.
+    """
+    errs = _page_fp32_errors()
+    N = 1024
+    g = torch.Generator().manual_seed(1)
+    q, k, v = (torch.randn(1, 8, N, 64, generator=g) for _ in range(3))
+    got = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    o, _ = oracle.forward(q.double().numpy(), k.double().numpy(), v.double().numpy(), None, True)
+    err = np.max(np.abs(got.double().numpy() - o))
+    assert err < 10 * errs[N], err
+
+
+# ------------------------------------------------------------ mutation test ---
+
+MUTANTS = {
+    "no_scale": ("s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T)"),
+    "mask_excludes_diagonal": ("cols <= rows", "cols < rows"),
+    "mask_one_too_many": ("cols <= rows", "cols <= rows + 1"),
+    "lse_missing_log_l": ("lse = (m + np.log(l))[:, 0]", "lse = m[:, 0]"),
+    "lse_log2": ("lse = (m + np.log(l))[:, 0]", "lse = (m + np.log2(l))[:, 0]"),
+    "softmax_no_normalise": ("p = e / l", "p = e"),
+    "gqa_modulo_map": ("return h // (H // H_kv)", "return h % H_kv"),
+    "pv_uses_k": ("o[r0:r0 + ROW_BLOCK] = p @ v", "o[r0:r0 + ROW_BLOCK] = p @ k[:, :v.shape[1]]"),
+    "ds_missing_rowdot": ("ds = p * (dp - row_dot)", "ds = p * dp"),
+    "ds_sign": ("ds = p * (dp - row_dot)", "ds = p * (row_dot - dp)"),
+    "dq_missing_scale": ("dq[rid] = scale * (ds @ k)", "dq[rid] = (ds @ k)"),
+    "dq_uses_v": ("dq[rid] = scale * (ds @ k)", "dq[rid] = scale * (ds @ v)"),
+    "dk_missing_scale": ("dk += scale * (ds.T @ q[rid])", "dk += (ds.T @ q[rid])"),
+    "dv_uses_ds": ("dv += p.T @ do[rid]", "dv += ds.T @ do[rid]"),
+    "gqa_grads_overwrite": ("dk[b, kv] += gk", "dk[b, kv] = gk"),
+}
+
+
+def _mutant_module(old, new):
+    src = open(oa.__file__).read()
+    assert old in src, f"mutation anchor missing: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    mod = _mutant_module(*MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
