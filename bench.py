@@ -1,0 +1,302 @@
+"""Attention throughput on one MI355X: TFLOP/s (causal-adjusted) and % of MFMA peak.
+
+One step = one forward pass over every case of the bf16 forward problem
+(B=1, H=8, N=8192, d=64, causal and non-causal, plus its d=256 variant at
+B=8, H=16, N=2048, causal), inputs resident in HBM.  FLOPs follow the
+standard count: 4*B*H*N^2*d per forward, halved exactly when causal.
+
+The JSON line also carries:
+  roofline      the dominant kernel's algorithmic TFLOP/s (from HIP events
+                around each of its launches inside the timed region) against
+                the dense bf16 MFMA peak, and its HBM traffic per launch from
+                the committed rocprofv3 counter summary when that summary was
+                taken on the current kernel source (else null);
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload on this host's cores;
+  extra         the other kernels measured the same way: the headline-size
+                causal bf16 d=128 forward, the fp32 and fp8 forwards, and the
+                bf16 backward (fwd+bwd) at its full size.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # dense MFMA, 256 CU x 2.4 GHz
+HBM_GBS = 8000.0
+STEP = ["C2a", "C2a_nc", "C2b"]
+EXTRA_FWD = ["Ta", "Ta_gqa", "Tb", "Tc", "C1", "C3", "C5"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default=None, help="time one workload alone (profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+class Case:
+    """Device-resident inputs of one workload and a launcher for its kernels."""
+
+    def __init__(self, name, dev, backward=False):
+        import torch
+        import synthetic as syn
+        self.w = syn.WORKLOADS[name]
+        x = syn.make_inputs(self.w, with_do=backward)
+        self.scale = x["scale"]
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.sc = {}
+        if x["q_scale"] is not None:
+            self.sc = dict(q_descale=x["q_scale"].to(dev), k_descale=x["k_scale"].to(dev),
+                           v_descale=x["v_scale"].to(dev))
+        B, H, N, d = self.w.B, self.w.H, self.w.N, self.w.d
+        odt = torch.float32 if self.w.dtype == "f32" else torch.bfloat16
+        self.o = torch.empty(B, H, N, d, device=dev, dtype=odt)
+        self.lse = torch.empty(B, H, N, device=dev, dtype=torch.float32)
+        self.backward = backward
+        if backward:
+            import exact_tiled_attention_amd as fa
+            self.do = x["do"].to(dev)
+            self.dq = torch.empty_like(self.q)
+            self.dk = torch.empty_like(self.k)
+            self.dv = torch.empty_like(self.v)
+            need = fa.fa_bwd_workspace_bytes(B, H, self.w.H_kv, N, d, 1)
+            self.ws = torch.empty(need, device=dev, dtype=torch.uint8)
+
+    def fwd(self):
+        import exact_tiled_attention_amd as fa
+        fa.fa_fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.scale,
+                  out=self.o, lse=self.lse, **self.sc)
+
+    def bwd(self):
+        import exact_tiled_attention_amd as fa
+        fa.fa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.w.causal,
+                  scale=self.scale, workspace=self.ws, dq=self.dq, dk=self.dk, dv=self.dv)
+
+
+def kernel_name(w, direction="fwd"):
+    if direction == "bwd":
+        return f"bwd_bf16_d{w.d}_{'causal' if w.causal else 'full'}"
+    return f"fwd_{w.dtype}_d{w.d}_{'causal' if w.causal else 'full'}"
+
+
+def time_launches(fn, reps, warmup):
+    """Per-launch durations (ms) from HIP events on the launching stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if t.get("source_hash") != source_hash():
+        return {}
+    return t.get("kernels", {})
+
+
+def cpu_baseline(budget_s=20.0):
+    """The oracle on a bounded sample: whole rows of the step's workloads."""
+    import numpy as np
+    import oracle
+    import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    flops = 0.0
+    t_total = 0.0
+    done = []
+    per_case = budget_s / len(STEP)
+    for name in STEP:
+        w = syn.WORKLOADS[name]
+        x = syn.make_inputs(w, with_do=False)          # the step's own inputs, as the GPU sees them
+        rows_done = heads = 0
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.H):
+                if time.perf_counter() - t0 >= per_case:
+                    break
+                kv = oracle.kv_head_of(h, w.H, w.H_kv)
+                rows = np.arange(w.N)
+                oracle.forward_rows(x["q_64"][b, h], x["k_64"][b, kv], x["v_64"][b, kv],
+                                    x["scale"], w.causal, rows)
+                vis = (rows + 1) if w.causal else np.full(rows.size, w.N)
+                flops += float(np.sum(4.0 * w.d * vis))
+                rows_done += rows.size
+                heads += 1
+        t_total += time.perf_counter() - t0
+        done.append(f"{name}: {heads} of {w.B * w.H} heads")
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "fp64 numpy oracle over whole heads (all rows, all visible keys) of each step "
+                      "workload, heads taken in order until a per-workload time budget; " + "; ".join(done)
+                      + f"; {t_total:.1f} s; TFLOP/s counts 4*d per visible (query,key) pair"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    import exact_tiled_attention_amd as fa
+    fa.load_library()
+
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+
+    names = [args.only] if args.only else STEP
+    cases = [Case(n, dev) for n in names]
+    step_flops = sum(c.w.flops_fwd() for c in cases)
+
+    def step():
+        for c in cases:
+            c.fwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    per = {c.w.name: [] for c in cases}
+    ev = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(st)
+    for _ in range(args.steps):
+        for c in cases:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            c.fwd()
+            b.record(st)
+            ev.append((c.w.name, a, b))
+    t_end.record(st)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    for name, a, b in ev:
+        per[name].append(a.elapsed_time(b))
+    ms_per_step = total_ms / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: most time inside the timed region
+    dom = max(cases, key=lambda c: sum(per[c.w.name]))
+    dom_ms = sum(per[dom.w.name]) / len(per[dom.w.name])
+    achieved = dom.w.flops_fwd() / (dom_ms * 1e-3) / 1e12
+    traffic = load_traffic().get(kernel_name(dom.w))
+    roofline = {"bound": "mfma", "kernel": kernel_name(dom.w), "workload": dom.w.name,
+                "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dom.w.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[dom.w.dtype], 4),
+                "avg_launch_ms": round(dom_ms, 4),
+                "traffic": traffic}
+    cases_out = {c.w.name: {"ms_median": round(median(per[c.w.name]), 4),
+                            "tflops": round(c.w.flops_fwd() / (median(per[c.w.name]) * 1e-3) / 1e12, 2)}
+                 for c in cases}
+
+    extra = {}
+    if not args.no_extra and not args.only:
+        del cases
+        torch.cuda.empty_cache()
+        for name in EXTRA_FWD:
+            c = Case(name, dev)
+            ms = median(time_launches(c.fwd, reps=10, warmup=2))
+            tf = c.w.flops_fwd() / (ms * 1e-3) / 1e12
+            extra[name] = {"kernel": kernel_name(c.w), "ms": round(ms, 4), "tflops": round(tf, 2),
+                           "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
+            del c
+            torch.cuda.empty_cache()
+        c = Case("C4", dev, backward=True)
+        ms_f = median(time_launches(c.fwd, reps=10, warmup=2))
+        ms_b = median(time_launches(c.bwd, reps=10, warmup=2))
+        extra["C4"] = {"fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+                       "fwd_tflops": round(c.w.flops_fwd() / (ms_f * 1e-3) / 1e12, 2),
+                       "bwd_tflops": round(c.w.flops_bwd() / (ms_b * 1e-3) / 1e12, 2),
+                       "fwd_bwd_tflops": round((c.w.flops_fwd() + c.w.flops_bwd())
+                                               / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
+                       "bwd_frac_peak": round(c.w.flops_bwd() / (ms_b * 1e-3) / 1e12
+                                              / PEAK_TFLOPS["bf16"], 4)}
+        del c
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (causal-adjusted) and % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, bf16 RNE)",
+        "config": {"workload": "bf16 forward: B=1,H=8,N=8192,d=64 causal + non-causal; "
+                               "B=8,H=16,N=2048,d=256 causal" if not args.only else args.only,
+                   "cases": cases_out, "frac_of_bf16_peak": round(value / PEAK_TFLOPS["bf16"], 4),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

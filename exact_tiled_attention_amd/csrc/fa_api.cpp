@@ -1,0 +1,151 @@
+// The C ABI of libfa.so: argument validation, then one launch sequence on the
+// caller's stream.  Validation finishes before any HIP runtime call, so every
+// error code can be produced without a device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int kMaxN = 1 << 28;
+
+size_t elem_bytes(fa_dtype t) { return t == FA_DTYPE_F32 ? 4 : (t == FA_DTYPE_BF16 ? 2 : 1); }
+size_t out_bytes(fa_dtype t) { return t == FA_DTYPE_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool valid_dtype(int t) { return t == FA_DTYPE_F32 || t == FA_DTYPE_BF16 || t == FA_DTYPE_FP8_E4M3; }
+
+// Shape checks shared by both directions; also guards every size product.
+fa_status check_shape(int B, int H, int H_kv, int N, int d) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_SHAPE;
+  if (H % H_kv != 0) return FA_ERR_INVALID_SHAPE;
+  if (N > kMaxN) return FA_ERR_INVALID_SHAPE;
+  const unsigned long long rows = (unsigned long long)B * H * N;
+  if (rows > (1ull << 40) || rows * (unsigned long long)d > (1ull << 44)) return FA_ERR_INVALID_SHAPE;
+  // grid sizes (work items of 32-row tiles at worst) must fit a 32-bit int
+  if ((unsigned long long)B * H * ((N + 31) / 32) > 0x7fffffffull) return FA_ERR_INVALID_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_supported(fa_dtype dtype, int d, int backward) {
+  if (!valid_dtype(dtype)) return 0;
+  if (backward) return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128);
+  switch (dtype) {
+    case FA_DTYPE_F32: return d == 64;
+    case FA_DTYPE_BF16: return d == 64 || d == 128 || d == 256;
+    case FA_DTYPE_FP8_E4M3: return d == 128;
+  }
+  return 0;
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
+    case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: non-positive size, H not a multiple of H_kv, or size overflow";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this (dtype, head dim, direction)";
+    case FA_ERR_INVALID_VALUE: return "FA_ERR_INVALID_VALUE: non-finite scale, misaligned pointer, aliasing output, or misplaced descale";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error at launch";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 int B, int H, int H_kv, int N, int d, float scale, int causal,
+                 fa_dtype dtype, hipStream_t stream) {
+  if (!Q || !K || !V || !O) return FA_ERR_NULL_POINTER;
+  if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
+  const bool fp8 = dtype == FA_DTYPE_FP8_E4M3;
+  if (fp8 && (!q_descale || !k_descale || !v_descale)) return FA_ERR_NULL_POINTER;
+  if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
+  if (!fa_supported(dtype, d, 0)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_INVALID_VALUE;
+  if (!fp8 && (q_descale || k_descale || v_descale)) return FA_ERR_INVALID_VALUE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_INVALID_VALUE;
+  if (fp8 && (!aligned16(q_descale) || !aligned16(k_descale) || !aligned16(v_descale)))
+    return FA_ERR_INVALID_VALUE;
+  const size_t nq = (size_t)B * H * N * d, nkv = (size_t)B * H_kv * N * d;
+  const size_t ob = nq * out_bytes(dtype), lb = LSE ? (size_t)B * H * N * 4 : 0;
+  const size_t eb = elem_bytes(dtype);
+  if (overlap(O, ob, Q, nq * eb) || overlap(O, ob, K, nkv * eb) || overlap(O, ob, V, nkv * eb) ||
+      overlap(LSE, lb, Q, nq * eb) || overlap(LSE, lb, K, nkv * eb) || overlap(LSE, lb, V, nkv * eb) ||
+      overlap(LSE, lb, O, ob))
+    return FA_ERR_INVALID_VALUE;
+
+  fa::FwdParams p{};
+  p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE;
+  p.qs = q_descale; p.ks = k_descale; p.vs = v_descale;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e;
+  switch (dtype) {
+    case FA_DTYPE_F32: e = fa::launch_fwd_f32(d, causal != 0, p, stream); break;
+    case FA_DTYPE_BF16: e = fa::launch_fwd_bf16(d, causal != 0, p, stream); break;
+    default: e = fa::launch_fwd_fp8(d, causal != 0, p, stream); break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dtype) {
+  if (!valid_dtype(dtype) || check_shape(B, H, H_kv, N, d) != FA_OK) return 0;
+  const size_t delta = (size_t)B * H * N * sizeof(float);
+  return (delta + 255) & ~(size_t)255;
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                 size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
+                 int causal, fa_dtype dtype, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL_POINTER;
+  if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
+  if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
+  if (!fa_supported(dtype, d, 1)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_INVALID_VALUE;
+  const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return FA_ERR_INVALID_VALUE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, H_kv, N, d, dtype);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return FA_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(dtype);
+  const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
+  const size_t nl = (size_t)B * H * N * 4;
+  const void* ins[] = {Q, K, V, O, LSE, dO};
+  const size_t insz[] = {nq, nkv, nkv, nq, nl, nq};
+  void* outs[] = {dQ, dK, dV, workspace};
+  const size_t outsz[] = {nq, nkv, nkv, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_VALUE;
+  }
+
+  fa::BwdParams p{};
+  p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE; p.dout = dO;
+  p.dq = dQ; p.dk = dK; p.dv = dV;
+  p.delta = (float*)workspace;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_bwd_bf16(d, causal != 0, p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

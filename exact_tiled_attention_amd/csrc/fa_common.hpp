@@ -1,0 +1,100 @@
+// Device helpers shared by the gfx950 attention kernels: MFMA wrappers,
+// bf16/fp8 packing, cross-half-wave exchange and the work-item map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// The running max is only moved when a tile's max exceeds it by more than
+// this many powers of two, so most tiles skip the rescale of the output;
+// probabilities then stay below 2^kRescaleSlack, far inside fp32/bf16 range.
+constexpr float kRescaleSlack = 8.0f;
+
+// ---------------------------------------------------------------- MFMA ----
+// 32x32 output tile, fp32 accumulate.  Output layout (all 32x32 shapes):
+// lane l holds column (l & 31); register r holds row 8*(r/4) + 4*(l/32) + r%4.
+// Operand layout: lane l holds row/column (l & 31) and k-slots
+// [(l/32)*KL, (l/32)*KL + KL) where KL is the per-lane k count; A and B use
+// the same slot numbering, so any consistent slot->k map gives the same sum.
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// 32x32x64 fp8 (OCP e4m3) x fp8; 32 codes per lane per operand.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------- conversions ---
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (bf16)lo;
+  v[1] = (bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)p[i];
+  return v;
+}
+// Two bf16 halves taken from the low (sel=0) or high (sel=1) 16 bits of a and b.
+__device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
+  // result = (b.lo16 << 16) | a.lo16
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
+  // result = (b.hi16 << 16) | a.hi16
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---------------------------------------------------------- exchanges -----
+// Swap a value between lane l and lane l^32 (the two halves of a wave hold
+// different keys of the same query row).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ----------------------------------------------------------- work map -----
+// Work item -> (head, q-tile).  Workgroups are handed to the 8 XCDs round
+// robin (id % 8), each XCD with its own L2.  When the item count divides by
+// 8 the map gives each XCD a contiguous range of items, so the q-tiles of one
+// head run on one XCD and share that head's K/V in its L2.  Inside a head the
+// heaviest causal tiles (largest q-tile index) are issued first.
+struct WorkItem {
+  int bh;
+  int qt;
+};
+__device__ __forceinline__ WorkItem map_work(int block, int total, int n_qt, bool remap) {
+  int w = block;
+  if (remap) {
+    const int per = total >> 3;
+    w = (block & 7) * per + (block >> 3);
+  }
+  WorkItem it;
+  it.bh = w / n_qt;
+  it.qt = n_qt - 1 - (w - it.bh * n_qt);
+  return it;
+}
+
+}  // namespace fa

@@ -1,0 +1,545 @@
+// Forward attention kernels for gfx950 (bf16 / fp8 MFMA and fp32 MFMA).
+//
+// One workgroup owns BR consecutive query rows of one head and streams the
+// head's K/V tiles (BC keys each) through LDS, double buffered: the global
+// loads of tile j+1 are issued before tile j is consumed and land in the
+// other LDS buffer afterwards.  This is the tiling of "FlashAttentionとは？…"
+// (QKVをブロック分割してSRAMへ載せるタイリングの手順) with the loop order of
+// FlashAttention-2 (queries outside, keys inside; parallel over query tiles,
+// "Flash Attention 2 / 3 とは 2026年版", FA2 の改善): the output accumulator
+// never leaves registers until the epilogue.
+//
+// Each wave owns 32 query rows.  Scores are computed transposed,
+// S^T = K Q^T, so that in the MFMA output layout one lane holds one query
+// row (16 keys per 32-key block, the other 16 in lane l^32): the row max and
+// row sum need one cross-half exchange instead of a 32-lane reduction.  The
+// probabilities then feed O^T += V^T P^T directly as the B operand, with V
+// staged transposed in LDS.
+//
+// Online softmax ("FlashAttentionとは？…", 最大値と正規化項を持ち回るオンライン
+// softmaxの再スケール): running max m and running sum l per row; exp2 with
+// scale*log2(e) folded into one FMA; 1/l applied once in the epilogue.  The
+// rescale of the accumulator is skipped unless a tile's max exceeds m by more
+// than kRescaleSlack (a wave-uniform test), which keeps the result exact up
+// to rounding because m only has to bound the scores, not equal their max.
+//
+// Causal: key tiles past the work-group's last query are never loaded; the
+// mask is applied only on tiles that straddle the diagonal or the sequence
+// end (FA2's causal optimisation, "Flash Attention 2 / 3 とは 2026年版").
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// ===================================================== bf16 / fp8 ========
+template <int D, bool CAUSAL, bool FP8>
+struct FwdCfg {
+  static constexpr int NW = 4;              // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;        // query rows per workgroup
+  static constexpr int BC = 64;             // keys per tile
+  static constexpr int QE = FP8 ? 1 : 2;    // bytes per Q/K/V element
+  static constexpr int KSB = D * QE + 16;   // K row stride in LDS (bytes)
+  static constexpr int VS = BC + 4;         // V^T row stride in LDS (bf16 elements)
+  static constexpr int KBUF = BC * KSB;     // bytes
+  static constexpr int VBUF = D * VS * 2;   // bytes
+  static constexpr int BUF = KBUF + VBUF;
+  static constexpr int CPR = D * QE / 16;   // 16-byte chunks per K/V row
+  static constexpr int KCH = BC * CPR / NT; // K chunks per thread
+  static constexpr int VE = 16 / QE;        // elements per 16-byte V chunk
+  static constexpr int NVB = (BC / 4) * (D / VE);   // V blocks of 4 keys x VE cols
+  static constexpr int VBT = (NVB + NT - 1) / NT;   // V blocks per thread
+  static_assert(BC * CPR % NT == 0, "K tile must split evenly");
+};
+
+template <int D, bool CAUSAL, bool FP8>
+__global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
+  using C = FwdCfg<D, CAUSAL, FP8>;
+  constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int kvh = h / (p.H / p.H_kv);
+  const int bkv = b * p.H_kv + kvh;
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * D * C::QE;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * D * C::QE;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * D * C::QE;
+
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;        // this wave's first query
+  const int myq = q0 + lr;                  // this lane's query row
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  // ---- Q operand (B of S^T = K Q^T), resident in registers -----------------
+  // bf16: slot (kb, g, e) <-> column kb*16 + 8g + e; fp8: kb*64 + 32g + e.
+  constexpr int QREGS = FP8 ? D / 64 : D / 16;
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type qop_t;
+  qop_t qr[QREGS];
+#pragma unroll
+  for (int kb = 0; kb < QREGS; ++kb) {
+    if constexpr (FP8) {
+      i32x8 x = {};
+      if (myq < N) {
+        const i32x4* src = (const i32x4*)(qg + (size_t)myq * D + kb * 64 + 32 * g);
+        i32x4 lo = src[0], hi = src[1];
+        x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      qr[kb] = x;
+    } else {
+      bf16x8 x = {};
+      if (myq < N) x = *(const bf16x8*)(qg + ((size_t)myq * D + kb * 16 + 8 * g) * 2);
+      qr[kb] = x;
+    }
+  }
+
+  float c_base = p.scale_log2;
+  if constexpr (FP8) c_base *= p.qs[(size_t)wi.bh * ((N + 127) >> 7) + (q_first >> 7)];
+  const float* ksc = FP8 ? p.ks + (size_t)bkv * ((N + 127) >> 7) : nullptr;
+  const float* vsc = FP8 ? p.vs + (size_t)bkv * ((N + 127) >> 7) : nullptr;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // ---- tile staging: global -> registers -> LDS ----------------------------
+  i32x4 kreg[C::KCH];
+  i32x4 vreg[C::VBT][4];
+  auto load_tile = [&](int j) {
+    const int key0 = j * BC;
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int c = tid + it * NT;
+      const int row = c / C::CPR, col = c - row * C::CPR;
+      const int key = key0 + row;
+      i32x4 x = {};
+      if (key < N) x = *(const i32x4*)(kg + ((size_t)key * D * C::QE + col * 16));
+      kreg[it] = x;
+    }
+#pragma unroll
+    for (int it = 0; it < C::VBT; ++it) {
+      const int blk = tid + it * NT;
+      const int kq = blk % (BC / 4), cc = blk / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + kq * 4 + r;
+        i32x4 x = {};
+        if (blk < C::NVB && key < N) x = *(const i32x4*)(vg + ((size_t)key * D * C::QE + cc * 16));
+        vreg[it][r] = x;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* kl = smem + buf * C::BUF;
+    bf16* vt = (bf16*)(kl + C::KBUF);
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int c = tid + it * NT;
+      const int row = c / C::CPR, col = c - row * C::CPR;
+      *(i32x4*)(kl + row * C::KSB + col * 16) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VBT; ++it) {
+      const int blk = tid + it * NT;
+      if (blk < C::NVB) {
+        const int kq = blk % (BC / 4), cc = blk / (BC / 4);
+        if constexpr (FP8) {
+          // 16 fp8 columns per chunk -> bf16 (exact: e4m3 has 3 fraction bits)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int hw = 0; hw < 2; ++hw) {
+              float f[4][2];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                auto t = hw ? __builtin_amdgcn_cvt_pk_f32_fp8(vreg[it][r][w], true)
+                            : __builtin_amdgcn_cvt_pk_f32_fp8(vreg[it][r][w], false);
+                f[r][0] = t[0];
+                f[r][1] = t[1];
+              }
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int col = cc * 16 + w * 4 + hw * 2 + e;
+                uint32_t lo = pack_bf16(f[0][e], f[1][e]);
+                uint32_t hi = pack_bf16(f[2][e], f[3][e]);
+                *(i32x2*)(vt + col * C::VS + kq * 4) = i32x2{(int)lo, (int)hi};
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t a0 = vreg[it][0][w], a1 = vreg[it][1][w];
+            const uint32_t a2 = vreg[it][2][w], a3 = vreg[it][3][w];
+            const int col = cc * 8 + w * 2;
+            *(i32x2*)(vt + col * C::VS + kq * 4) =
+                i32x2{(int)perm_lo16(a0, a1), (int)perm_lo16(a2, a3)};
+            *(i32x2*)(vt + (col + 1) * C::VS + kq * 4) =
+                i32x2{(int)perm_hi16(a0, a1), (int)perm_hi16(a2, a3)};
+          }
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    __syncthreads();
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const int key0 = j * BC;
+    // Waves whose rows all precede this tile see none of its keys.
+    const bool active = !CAUSAL || key0 <= q0 + 31;
+    if (active) {
+      const unsigned char* kl = smem + (j & 1) * C::BUF;
+      const bf16* vt = (const bf16*)(kl + C::KBUF);
+      // ---- S^T = K Q^T ------------------------------------------------------
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+        f32x16 acc = {};
+        const unsigned char* krow = kl + (kb32 * 32 + lr) * C::KSB;
+#pragma unroll
+        for (int kb = 0; kb < QREGS; ++kb) {
+          if constexpr (FP8) {
+            const i32x4* src = (const i32x4*)(krow + kb * 64 + 32 * g);
+            i32x4 lo = src[0], hi = src[1];
+            i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = mfma_fp8(a, qr[kb], acc);
+          } else {
+            bf16x8 a = *(const bf16x8*)(krow + (kb * 16 + 8 * g) * 2);
+            acc = mfma_bf16(a, qr[kb], acc);
+          }
+        }
+        s[kb32] = acc;
+      }
+      // ---- mask (diagonal / tail tiles only) -------------------------------
+      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+          }
+      }
+      // ---- online softmax ----------------------------------------------------
+      float c = c_base;
+      if constexpr (FP8) c *= ksc[key0 >> 7];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_cand = mx * c;
+      if (__any(m_cand > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+      float madj = m_run;
+      float inv_sv = 1.f;
+      if constexpr (FP8) {
+        const float sv = vsc[key0 >> 7];
+        madj -= fast_log2(sv);   // p' = p * sV folds V's block scale into P
+        inv_sv = 1.f / sv;
+      }
+      float ts = 0.f;
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(s[kb32][r], c, -madj));
+          s[kb32][r] = e;
+          ts += e;
+        }
+      l_run += FP8 ? ts * inv_sv : ts;
+      // ---- O^T += V^T P^T ----------------------------------------------------
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = s[kb32][half * 8 + e];
+          const bf16x8 pb = pack_bf16x8(pv);
+          const int kcol = kb32 * 32 + 16 * half + 4 * g;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16* vrow = vt + (db * 32 + lr) * C::VS + kcol;
+            const bf16x4 lo = *(const bf16x4*)vrow;
+            const bf16x4 hi = *(const bf16x4*)(vrow + 8);
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[db] = mfma_bf16(a, pb, o[db]);
+          }
+        }
+    }
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+  }
+
+  // ---- epilogue: O = acc / l, LSE = m + log2(l) in natural-log units --------
+  const float l_tot = l_run + swap_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ========================================================== fp32 ==========
+// fp32 inputs on the fp32 MFMA (32x32x2); probabilities stay fp32.
+template <int D, bool CAUSAL, int NW>
+struct F32Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;
+  static constexpr int BC = 64;
+  static constexpr int KS = D + 4;          // K row stride (floats)
+  static constexpr int VS = BC + 4;         // V^T row stride (floats)
+  static constexpr int KBUF = BC * KS;      // floats
+  static constexpr int VBUF = D * VS;
+  static constexpr int BUF = KBUF + VBUF;
+  static constexpr int CPR = D / 4;         // 16-byte chunks per row
+  static constexpr int KCH = BC * CPR / NT;
+  static constexpr int NVB = (BC / 4) * (D / 4);
+  static constexpr int VBT = NVB / NT;
+  static_assert(BC * CPR % NT == 0 && NVB % NT == 0, "tile must split evenly");
+};
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdParams p) {
+  using C = F32Cfg<D, CAUSAL, NW>;
+  constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) float smem[2 * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const float* qg = (const float*)p.q + (size_t)wi.bh * N * D;
+  const float* kg = (const float*)p.k + (size_t)bkv * N * D;
+  const float* vg = (const float*)p.v + (size_t)bkv * N * D;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  // slot (kb4, e, g) <-> column kb4*8 + 4g + e
+  f32x4 qr[D / 8];
+#pragma unroll
+  for (int kb = 0; kb < D / 8; ++kb) {
+    f32x4 x = {};
+    if (myq < N) x = *(const f32x4*)(qg + (size_t)myq * D + kb * 8 + 4 * g);
+    qr[kb] = x;
+  }
+  const float c = p.scale_log2;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  f32x4 kreg[C::KCH];
+  f32x4 vreg[C::VBT][4];
+  auto load_tile = [&](int j) {
+    const int key0 = j * BC;
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int cidx = tid + it * NT;
+      const int row = cidx / C::CPR, col = cidx - row * C::CPR;
+      f32x4 x = {};
+      if (key0 + row < N) x = *(const f32x4*)(kg + (size_t)(key0 + row) * D + col * 4);
+      kreg[it] = x;
+    }
+#pragma unroll
+    for (int it = 0; it < C::VBT; ++it) {
+      const int blk = tid + it * NT;
+      const int kq = blk % (BC / 4), cc = blk / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + kq * 4 + r;
+        f32x4 x = {};
+        if (key < N) x = *(const f32x4*)(vg + (size_t)key * D + cc * 4);
+        vreg[it][r] = x;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    float* kl = smem + buf * C::BUF;
+    float* vt = kl + C::KBUF;
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int cidx = tid + it * NT;
+      const int row = cidx / C::CPR, col = cidx - row * C::CPR;
+      *(f32x4*)(kl + row * C::KS + col * 4) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VBT; ++it) {
+      const int blk = tid + it * NT;
+      const int kq = blk % (BC / 4), cc = blk / (BC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(f32x4*)(vt + (cc * 4 + e) * C::VS + kq * 4) =
+            f32x4{vreg[it][0][e], vreg[it][1][e], vreg[it][2][e], vreg[it][3][e]};
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    __syncthreads();
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const int key0 = j * BC;
+    const bool active = !CAUSAL || key0 <= q0 + 31;
+    if (active) {
+      const float* kl = smem + (j & 1) * C::BUF;
+      const float* vt = kl + C::KBUF;
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+        f32x16 acc = {};
+        const float* krow = kl + (kb32 * 32 + lr) * C::KS + 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < D / 8; ++kb) {
+          const f32x4 a = *(const f32x4*)(krow + kb * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], qr[kb][e], acc);
+        }
+        s[kb32] = acc;
+      }
+      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_cand = mx * c;
+      if (__any(m_cand > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+      float ts = 0.f;
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(s[kb32][r], c, -m_run));
+          s[kb32][r] = e;
+          ts += e;
+        }
+      l_run += ts;
+      // O^T += V^T P^T: MFMA (kb32, r) takes key kb32*32 + 8*(r/4) + 4g + r%4
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const f32x4 va = *(const f32x4*)(vt + (db * 32 + lr) * C::VS + kb32 * 32 + 8 * a4 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db] = mfma_f32(va[e], s[kb32][4 * a4 + e], o[db]);
+          }
+    }
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    float* orow = (float*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4*)(orow + db * 32 + 8 * a + 4 * g) =
+            f32x4{o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
+                  o[db][4 * a + 3] * inv};
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ========================================================= launchers ======
+static void finish_grid(FwdParams& p, int br) {
+  p.n_qt = (p.N + br - 1) / br;
+  p.total = p.B * p.H * p.n_qt;
+  p.remap = (p.total % 8 == 0) ? 1 : 0;
+}
+
+template <int D, bool CAUSAL, bool FP8>
+static hipError_t launch_mfma(FwdParams& p, hipStream_t s) {
+  finish_grid(p, FwdCfg<D, CAUSAL, FP8>::BR);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, CAUSAL, FP8>), dim3(p.total), dim3(FwdCfg<D, CAUSAL, FP8>::NT),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
+  switch (d) {
+    case 64: return causal ? launch_mfma<64, true, false>(p, s) : launch_mfma<64, false, false>(p, s);
+    case 128: return causal ? launch_mfma<128, true, false>(p, s) : launch_mfma<128, false, false>(p, s);
+    case 256: return causal ? launch_mfma<256, true, false>(p, s) : launch_mfma<256, false, false>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_fp8(int d, bool causal, FwdParams& p, hipStream_t s) {
+  if (d == 128) return causal ? launch_mfma<128, true, true>(p, s) : launch_mfma<128, false, true>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_f32(FwdParams& p, hipStream_t s) {
+  constexpr int NW = 2;
+  finish_grid(p, F32Cfg<D, CAUSAL, NW>::BR);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, NW>), dim3(p.total), dim3(F32Cfg<D, CAUSAL, NW>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(int d, bool causal, FwdParams& p, hipStream_t s) {
+  if (d == 64) return causal ? launch_f32<64, true>(p, s) : launch_f32<64, false>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library (libfa.so), gfx950.
+ *
+ * The library computes exact scaled dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * (the equation of "FlashAttention — フラッシュアテンション", section
+ * 標準的なアテンションの問題点) as fused, tiled kernels that never write the
+ * N x N score matrix to memory: K/V tiles stream through on-chip memory and a
+ * running row max and row sum of exponentials rescale the partial output
+ * whenever the max grows ("FlashAttentionとは？仕組みとFA2・FA3・FA4の違い…",
+ * section タイリング・オンラインsoftmax・再計算という3つの仕組み).  The forward
+ * saves one logsumexp per query row; the backward recomputes the probabilities
+ * from Q/K tiles with it instead of storing them (same page, subsection
+ * 逆伝播でL×L行列を保存せず再計算する設計).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory   All tensor pointers are DEVICE pointers owned by the caller.  The
+ *          library allocates and frees nothing, keeps no pointer after a call
+ *          returns and holds no mutable global state.
+ * Layout   Contiguous row-major, d innermost:
+ *            Q, O, dO, dQ    [B][H][N][d]
+ *            K, V, dK, dV    [B][H_kv][N][d]
+ *            LSE, D          [B][H][N]            (fp32)
+ *          Every base pointer must be 16-byte aligned.
+ * GQA      H must be a multiple of H_kv; query head h reads K/V head
+ *          h / (H / H_kv) (contiguous groups), as grouped-query attention is
+ *          described under FlashAttention-2 in "FlashAttention — フラッシュ
+ *          アテンション" (進化と関連技術).
+ * Causal   causal != 0 lets query i see keys 0..i (diagonal included).
+ * LSE      LSE[i] = ln sum_{j visible} exp(scale * q_i . k_j)  (natural log).
+ * Scale    any finite value; callers normally pass 1/sqrt(d).
+ * Streams  Work is enqueued on `stream` and runs asynchronously; device-side
+ *          faults surface at the caller's next synchronisation.
+ * Errors   Every entry point validates all arguments on the host before it
+ *          touches the HIP runtime and returns a status code; it never aborts
+ *          and never silently falls back to another implementation: an
+ *          unsupported (dtype, d, direction) combination is an error, as a
+ *          forced FLASH backend raises instead of falling back in the pages'
+ *          CPU SDPA experiment ("FlashAttentionとは？…", section CPUの
+ *          PyTorch SDPAで測った一致度とメモリ削減の実測値).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_F32 = 0,      /* fp32 in, fp32 out                                  */
+  FA_DTYPE_BF16 = 1,     /* bf16 in, bf16 out, fp32 accumulation               */
+  FA_DTYPE_FP8_E4M3 = 2  /* OCP e4m3 (max 448) Q/K/V + per-128-row fp32 scales,
+                            bf16 out                                           */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                       */
+  FA_ERR_INVALID_SHAPE = 2, /* B,H,H_kv,N,d <= 0; H % H_kv != 0; size overflow  */
+  FA_ERR_UNSUPPORTED = 3,   /* (dtype, d, direction) has no kernel              */
+  FA_ERR_INVALID_VALUE = 4, /* non-finite scale, misaligned pointer, an output
+                               aliasing an input, descale given for non-fp8    */
+  FA_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required          */
+  FA_ERR_HIP = 6            /* the HIP runtime reported an error at launch      */
+} fa_status;
+
+/*
+ * Forward pass.
+ *   Q [B][H][N][d], K/V [B][H_kv][N][d] in `dtype` (fp8: one byte per element).
+ *   O [B][H][N][d]: fp32 for F32, bf16 for BF16 and FP8_E4M3.
+ *   LSE [B][H][N] fp32, or NULL to skip it.
+ *   q_descale [B][H][ceil(N/128)], k_descale and v_descale [B][H_kv][ceil(N/128)]:
+ *     fp32 block scales, required for FP8_E4M3 and NULL otherwise; element
+ *     (b,h,n,:) of a tensor stands for code * descale[b][h][n/128].  This is
+ *     the block-wise quantisation with per-tile rescaling that "Flash
+ *     Attention 2 / 3 とは 2026年版" names for FP8 attention (section FA3 の
+ *     飛躍); the 128-row block is this library's choice.
+ * Supported: F32 d=64; BF16 d=64,128,256; FP8_E4M3 d=128.  Any N >= 1.
+ */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 int B, int H, int H_kv, int N, int d, float scale, int causal,
+                 fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem (0 on invalid
+ * arguments).  The workspace holds D = rowsum(dO * O) in fp32.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass by recomputation.
+ *   Q, K, V, O, dO as in the forward (O and LSE are the forward's outputs for
+ *   the same Q, K, V, scale and causal flag).  dQ, dK, dV have the layouts and
+ *   dtype of Q, K, V; dK/dV of a GQA group are summed over its query heads.
+ *   workspace: caller-owned device memory of at least
+ *   fa_bwd_workspace_bytes(...) bytes, 256-byte aligned; its contents on
+ *   entry do not matter and are garbage on return.
+ * Supported: BF16 d=64,128.  FP8 has no backward (FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                 size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
+                 int causal, fa_dtype dtype, hipStream_t stream);
+
+/* 1 if a kernel exists for (dtype, d, backward != 0), else 0. */
+int fa_supported(fa_dtype dtype, int d, int backward);
+
+/* Static, never-NULL description of a status code. */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,115 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry
+point, imports no allocator, and rejects every invalid argument before it
+touches the HIP runtime (so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_tiled_attention_amd import build
+        build.build(verbose=False)
+    return fa.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status|size_t|int|const char\*)\s+(fa_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(fa.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, re.M))
+    for name in _declared():
+        assert name in exported, name
+        getattr(lib, name)
+
+
+def test_library_never_allocates_device_memory():
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    for bad in ("hipMalloc", "hipFree", "hipMallocAsync", "hipHostMalloc", "hipMallocManaged"):
+        assert not re.search(rf"\b{bad}\b", out), bad
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = fa.fa_status_string(code)
+        assert s.startswith(fa.STATUS_NAMES[code])
+    assert fa.fa_status_string(99) == "unknown fa_status"
+
+
+def test_supported_table(lib):
+    assert fa.fa_supported(0, 64, False)
+    for d in (64, 128, 256):
+        assert fa.fa_supported(1, d, False)
+    assert fa.fa_supported(2, 128, False)
+    assert fa.fa_supported(1, 64, True) and fa.fa_supported(1, 128, True)
+    for dt, d, bwd in [(1, 96, False), (1, 192, False), (0, 128, False), (2, 64, False), (2, 128, True),
+                       (0, 64, True), (1, 256, True), (7, 64, False)]:
+        assert not fa.fa_supported(dt, d, bwd), (dt, d, bwd)
+
+
+P = 1 << 20  # a fake, 16-byte aligned address: validation rejects before any use
+
+
+def fwd(lib, q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, qs=None, ks=None, vs=None,
+        B=1, H=2, Hkv=2, N=16, d=64, scale=0.125, causal=1, dtype=1):
+    return lib.fa_fwd(q, k, v, o, lse, qs, ks, vs, B, H, Hkv, N, d, scale, causal, dtype, None)
+
+
+def bwd(lib, ws=64 * P, ws_bytes=1 << 20, d=64, dtype=1, N=16, H=2, Hkv=2, B=1, scale=0.125,
+        ptrs=None):
+    p = ptrs or [P * (i + 1) for i in range(9)]
+    return lib.fa_bwd(*p, ws, ws_bytes, B, H, Hkv, N, d, scale, 1, dtype, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == 1
+    assert fwd(lib, o=None) == 1
+    assert fwd(lib, dtype=2) == 1                    # fp8 without descales
+    assert fwd(lib, N=0) == 2
+    assert fwd(lib, B=-1) == 2
+    assert fwd(lib, H=6, Hkv=4) == 2                 # H % H_kv != 0
+    assert fwd(lib, N=1 << 29) == 2
+    assert fwd(lib, d=96) == 3                       # unsupported head dim
+    assert fwd(lib, d=128, dtype=0) == 3
+    assert fwd(lib, dtype=9) == 3
+    assert fwd(lib, scale=float("nan")) == 4
+    assert fwd(lib, scale=float("inf")) == 4
+    assert fwd(lib, qs=7 * P) == 4                   # descale on a non-fp8 call
+    assert fwd(lib, q=P + 8) == 4                    # misaligned
+    assert fwd(lib, lse=P + 4) == 4
+    assert fwd(lib, o=P) == 4                        # O aliases Q
+    assert fwd(lib, lse=4 * P + 64) == 4             # LSE inside O
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, ptrs=[None] + [P * (i + 2) for i in range(8)]) == 1
+    assert bwd(lib, dtype=2, d=128) == 3             # FP8 has no backward
+    assert bwd(lib, d=256) == 3
+    assert bwd(lib, N=0) == 2
+    assert bwd(lib, scale=float("nan")) == 4
+    assert bwd(lib, ws=None) == 5
+    assert bwd(lib, ws_bytes=16) == 5
+    assert bwd(lib, ws=64 * P + 128) == 5            # not 256-byte aligned
+    assert bwd(lib, ptrs=[P * (i + 1) for i in range(8)] + [P]) == 4   # dV aliases Q
+
+
+def test_workspace_bytes(lib):
+    assert fa.fa_bwd_workspace_bytes(2, 16, 16, 16384, 64) == 2 * 16 * 16384 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 3, 64) == 0
