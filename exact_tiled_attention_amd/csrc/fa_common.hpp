@@ -65,11 +65,17 @@ __device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
 }
 
 // ---------------------------------------------------------- exchanges -----
-// Swap a value between lane l and lane l^32 (the two halves of a wave hold
-// different keys of the same query row).
-__device__ __forceinline__ float swap_halves(float x) {
+// Combine a value across lane l and lane l^32 (the two halves of a wave hold
+// different keys of the same query row).  v_permlane32_swap with the same
+// register as both operands leaves, in every lane, its own value in one
+// result and its partner's in the other, so one op combines the pair.
+__device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
       for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = max_halves(mx);
       const float m_cand = mx * c;
       if (__any(m_cand > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, m_cand);
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = acc / l, LSE = m + log2(l) in natural-log units --------
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
     bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdParams p) {
       for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = max_halves(mx);
       const float m_cand = mx * c;
       if (__any(m_cand > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, m_cand);
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdParams p) {
     if (j + 1 < n_tiles) store_tile((j + 1) & 1);
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
     float* orow = (float*)p.o + ((size_t)wi.bh * N + myq) * D;
