@@ -59,7 +59,8 @@ struct DkdvCfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<D, CAUSAL>;
   constexpr int BKV = C::BKV, BQ = C::BQ, NT = C::NT;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_B];
@@ -295,7 +296,8 @@ struct DqCfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D, CAUSAL>;
   constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::BUF_E];

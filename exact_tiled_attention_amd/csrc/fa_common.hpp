@@ -78,6 +78,27 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ------------------------------------------------------------ LDS I/O -----
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// 16 bytes per lane straight from global memory into LDS (no registers).
+// The destination is wave-uniform: lane l's bytes land at lds + 16*l.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+// Transposing LDS read of 16-bit elements.  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive elements; lane i receives
+// element (i % 4) of the rows addressed by lanes 4j + i/4, j = 0..3.  With
+// lanes 4j+q pointing at row r0+j, columns c0+4q.., lane i gets column c0+i
+// of rows r0..r0+3: a 4 x 16 block arrives transposed.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds);
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

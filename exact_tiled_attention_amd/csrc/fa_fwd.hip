@@ -55,7 +55,10 @@ struct FwdCfg {
 };
 
 template <int D, bool CAUSAL, bool FP8>
-__global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdParams p) {
+  // Two waves per SIMD (<= 256 registers each) let one wave's softmax VALU
+  // work overlap the other wave's MFMAs; d = 256 cannot fit and runs at one.
   using C = FwdCfg<D, CAUSAL, FP8>;
   constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF];
@@ -311,6 +314,206 @@ __global__ __launch_bounds__(256) void fwd_mfma_kernel(FwdParams p) {
   }
 }
 
+// ====================================================== bf16, LDS DMA =====
+// The bf16 forward proper.  K and V tiles go straight from HBM to LDS
+// (global_load_lds: no staging registers, no VALU), unpadded and XOR-swizzled
+// per row so that the K operand reads (16 B per lane) and the transposing V
+// reads (ds_read_b64_tr_b16, which hands each lane a column of V) are free of
+// bank conflicts.  The two stages live in two distinct LDS arrays and the
+// tile loop is unrolled by two, so the compiler can see that the prefetch into
+// one stage never aliases the reads from the other.
+template <int D>
+struct Bf16Cfg {
+  static constexpr int NW = 4, NT = 256, BR = 128, BC = 64;
+  static constexpr int RB = D * 2;              // bytes per K/V row in LDS
+  static constexpr int TILE = BC * RB;          // bytes per K (or V) tile
+  static constexpr int IPW = TILE / 1024 / NW;  // 1 KB DMA issues per wave per tensor
+  static_assert(IPW >= 1, "tile too small for the DMA split");
+};
+// K row r keeps 16-byte unit u at position u ^ (r & 7); V row r at u ^ 2(r & 3).
+__device__ __forceinline__ int k_swz(int row, int u) { return u ^ (row & 7); }
+__device__ __forceinline__ int v_swz(int row, int u) { return u ^ ((row & 3) << 1); }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(FwdParams p) {
+  using C = Bf16Cfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * RB;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  // Q operand (B of S^T = K Q^T): slot (kb, g, e) <-> column kb*16 + 8g + e.
+  bf16x8 qr[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    bf16x8 x = {};
+    if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
+    qr[kb] = x;
+  }
+
+  // Per-lane byte offsets, fixed for the whole loop.
+  int dma_row[IPW], dma_k[IPW], dma_v[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_row[i] = row;
+    dma_k[i] = row * RB + k_swz(row, pu) * 16;   // the swizzle is an involution
+    dma_v[i] = row * RB + v_swz(row, pu) * 16;
+  }
+  int koff[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz(lr, 2 * kb + g) * 16;
+  const int s16 = lane & 15, G = lane >> 4;
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    voff[db] = vrow * RB + v_swz(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  const float c = p.scale_log2;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto issue = [&](int j, unsigned char* st) {
+    const int key0 = j * BC;
+    const unsigned char* kt = kg + (size_t)key0 * RB;
+    const unsigned char* vt = vg + (size_t)key0 * RB;
+    if (key0 + BC <= N) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        dma16(kt + dma_k[i], st + (wid * IPW + i) * 1024);
+        dma16(vt + dma_v[i], st + C::TILE + (wid * IPW + i) * 1024);
+      }
+    } else {
+      // tail tile: rows past the end re-read the last row (finite; masked later)
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int shift = (min(key0 + dma_row[i], N - 1) - key0 - dma_row[i]) * RB;
+        dma16(kt + dma_k[i] + shift, st + (wid * IPW + i) * 1024);
+        dma16(vt + dma_v[i] + shift, st + C::TILE + (wid * IPW + i) * 1024);
+      }
+    }
+  };
+
+  auto consume = [&](int j, const unsigned char* kl) {
+    const unsigned char* vl = kl + C::TILE;
+    const int key0 = j * BC;
+    if (CAUSAL && key0 > q0 + 31) return;   // every key of the tile follows every row of the wave
+    f32x16 s[BC / 32];
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + koff[kb]);
+        acc = mfma_bf16(a, qr[kb], acc);
+      }
+      s[kb32] = acc;
+    }
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+    mx = max_halves(mx);
+    const float m_cand = mx * c;
+    if (__any(m_cand > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    float ts = 0.f;
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[kb32][r], c, -m_run));
+        s[kb32][r] = e;
+        ts += e;
+      }
+    l_run += ts;
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = s[kb32][half * 8 + e];
+        const bf16x8 pb = pack_bf16x8(pv);
+        const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x4 lo = lds_read_tr16(vb + voff[db]);
+          const bf16x4 hi = lds_read_tr16(vb + 8 * RB + voff[db]);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[db]);
+        }
+      }
+  };
+
+  issue(0, stage0);
+  for (int j = 0; j < n_tiles; j += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, stage1);
+    consume(j, stage0);
+    if (j + 1 < n_tiles) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 2 < n_tiles) issue(j + 2, stage0);
+      consume(j + 1, stage1);
+    }
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
 // ========================================================== fp32 ==========
 // fp32 inputs on the fp32 MFMA (32x32x2); probabilities stay fp32.
 template <int D, bool CAUSAL, int NW>
@@ -515,11 +718,18 @@ static hipError_t launch_mfma(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
+  finish_grid(p, Bf16Cfg<D>::BR);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(Bf16Cfg<D>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_mfma<64, true, false>(p, s) : launch_mfma<64, false, false>(p, s);
-    case 128: return causal ? launch_mfma<128, true, false>(p, s) : launch_mfma<128, false, false>(p, s);
-    case 256: return causal ? launch_mfma<256, true, false>(p, s) : launch_mfma<256, false, false>(p, s);
+    case 64: return causal ? launch_bf16<64, true>(p, s) : launch_bf16<64, false>(p, s);
+    case 128: return causal ? launch_bf16<128, true>(p, s) : launch_bf16<128, false>(p, s);
+    case 256: return causal ? launch_bf16<256, true>(p, s) : launch_bf16<256, false>(p, s);
   }
   return hipErrorInvalidValue;
 }
