@@ -97,6 +97,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* lds) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds);
   return __builtin_bit_cast(bf16x4, v);
 }
+// The same DMA through a buffer resource: base and byte range in SGPRs, a
+// 32-bit per-lane offset; bytes past num_records read as zero, so a ragged
+// last tile needs no clamping and the address math costs no VALU work.
+// (The byte range is checked against the per-lane offset; the scalar offset
+// is always passed as 0.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num_bytes, 0x00020000);
+}
+template <int IMM>
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, IMM, 0);
+}
+// l += sum of the two bf16 halves of a packed pair (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

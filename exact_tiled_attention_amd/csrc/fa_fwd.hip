@@ -368,12 +368,11 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 
   // Per-lane byte offsets, fixed for the whole loop.
-  int dma_row[IPW], dma_k[IPW], dma_v[IPW];
+  int dma_k[IPW], dma_v[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int byte = (wid * IPW + i) * 1024 + lane * 16;
     const int row = byte / RB, pu = (byte % RB) / 16;
-    dma_row[i] = row;
     dma_k[i] = row * RB + k_swz(row, pu) * 16;   // the swizzle is an involution
     dma_v[i] = row * RB + v_swz(row, pu) * 16;
   }
@@ -395,22 +394,13 @@ void fwd_bf16_kernel(FwdParams p) {
 
   auto issue = [&](int j, unsigned char* st) {
     const int key0 = j * BC;
-    const unsigned char* kt = kg + (size_t)key0 * RB;
-    const unsigned char* vt = vg + (size_t)key0 * RB;
-    if (key0 + BC <= N) {
+    const int bytes = min(N - key0, BC) * RB;   // rows past the end read as zero
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        dma16(kt + dma_k[i], st + (wid * IPW + i) * 1024);
-        dma16(vt + dma_v[i], st + C::TILE + (wid * IPW + i) * 1024);
-      }
-    } else {
-      // tail tile: rows past the end re-read the last row (finite; masked later)
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int shift = (min(key0 + dma_row[i], N - 1) - key0 - dma_row[i]) * RB;
-        dma16(kt + dma_k[i] + shift, st + (wid * IPW + i) * 1024);
-        dma16(vt + dma_v[i] + shift, st + C::TILE + (wid * IPW + i) * 1024);
-      }
+    for (int i = 0; i < IPW; ++i) {
+      dma16_buf<0>(rk, dma_k[i], st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rv, dma_v[i], st + C::TILE + (wid * IPW + i) * 1024);
     }
   };
 
@@ -455,24 +445,30 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
+    // P in bf16 (the PV operand); the row sum is taken from the same rounded
+    // values, two at a time, so numerator and denominator use one P.
     float ts = 0.f;
+    bf16x8 pk[BC / 32][2];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(s[kb32][r], c, -m_run));
-        s[kb32][r] = e;
-        ts += e;
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m_run));
+          const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m_run));
+          w4[w] = pack_bf16(e0, e1);
+          ts = add_bf16_pair(w4[w], ts);
+        }
+        pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
       }
     l_run += ts;
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[kb32][half * 8 + e];
-        const bf16x8 pb = pack_bf16x8(pv);
+        const bf16x8 pb = pk[kb32][half];
         const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
