@@ -322,22 +322,33 @@ void fwd_mfma_kernel(FwdParams p) {
 // bank conflicts.  The two stages live in two distinct LDS arrays and the
 // tile loop is unrolled by two, so the compiler can see that the prefetch into
 // one stage never aliases the reads from the other.
-template <int D>
+template <int D, int NW_, int BC_>
 struct Bf16Cfg {
-  static constexpr int NW = 4, NT = 256, BR = 128, BC = 64;
+  static constexpr int NW = NW_, NT = NW * 64, BR = NW * 32, BC = BC_;
   static constexpr int RB = D * 2;              // bytes per K/V row in LDS
   static constexpr int TILE = BC * RB;          // bytes per K (or V) tile
   static constexpr int IPW = TILE / 1024 / NW;  // 1 KB DMA issues per wave per tensor
   static_assert(IPW >= 1, "tile too small for the DMA split");
 };
-// K row r keeps 16-byte unit u at position u ^ (r & 7); V row r at u ^ 2(r & 3).
-__device__ __forceinline__ int k_swz(int row, int u) { return u ^ (row & 7); }
-__device__ __forceinline__ int v_swz(int row, int u) { return u ^ ((row & 3) << 1); }
+// LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per clock and
+// an 8-byte read 32 lanes.  K operand reads put 16 consecutive rows on one
+// logical 16-byte unit, so K row r stores unit u at u ^ (r & 15) (rows of 128
+// bytes already alternate bank halves, so there u ^ ((r >> 1) & 7)).  The
+// transposing V reads put 4 consecutive rows x 4 units on one clock, so V row
+// r stores unit u at u ^ 4(r & 3) (128-byte rows: u ^ 4((r >> 1) & 1)).
+template <int RB>
+__device__ __forceinline__ int k_swz(int row, int u) {
+  return RB == 128 ? (u ^ ((row >> 1) & 7)) : (u ^ (row & 15));
+}
+template <int RB>
+__device__ __forceinline__ int v_swz(int row, int u) {
+  return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ ((row & 3) << 2));
+}
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int NW, int BC_>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
-  using C = Bf16Cfg<D>;
+  using C = Bf16Cfg<D, NW, BC_>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * C::TILE];
@@ -373,18 +384,18 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int i = 0; i < IPW; ++i) {
     const int byte = (wid * IPW + i) * 1024 + lane * 16;
     const int row = byte / RB, pu = (byte % RB) / 16;
-    dma_k[i] = row * RB + k_swz(row, pu) * 16;   // the swizzle is an involution
-    dma_v[i] = row * RB + v_swz(row, pu) * 16;
+    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;   // the swizzle is an involution
+    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
   }
   int koff[D / 16];
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz(lr, 2 * kb + g) * 16;
+  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
   const int s16 = lane & 15, G = lane >> 4;
   const int vrow = 4 * (G >> 1) + (s16 >> 2);
   int voff[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
-    voff[db] = vrow * RB + v_swz(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+    voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
 
   const float c = p.scale_log2;
   f32x16 o[D / 32];
@@ -714,18 +725,22 @@ static hipError_t launch_mfma(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NW, int BC>
 static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
-  finish_grid(p, Bf16Cfg<D>::BR);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(p.total), dim3(Bf16Cfg<D>::NT), 0, s, p);
+  using C = Bf16Cfg<D, NW, BC>;
+  finish_grid(p, C::BR);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
+// (waves, keys per tile) per head dim: d = 128 shares 128-key tiles among 8
+// waves (one 128 KB double-buffered stage set per CU); d = 64 and 256 keep
+// 4 waves and 64-key tiles.
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_bf16<64, true>(p, s) : launch_bf16<64, false>(p, s);
-    case 128: return causal ? launch_bf16<128, true>(p, s) : launch_bf16<128, false>(p, s);
-    case 256: return causal ? launch_bf16<256, true>(p, s) : launch_bf16<256, false>(p, s);
+    case 64: return causal ? launch_bf16<64, true, 4, 64>(p, s) : launch_bf16<64, false, 4, 64>(p, s);
+    case 128: return causal ? launch_bf16<128, true, 8, 128>(p, s) : launch_bf16<128, false, 8, 128>(p, s);
+    case 256: return causal ? launch_bf16<256, true, 4, 64>(p, s) : launch_bf16<256, false, 4, 64>(p, s);
   }
   return hipErrorInvalidValue;
 }
