@@ -31,6 +31,10 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
+#ifndef QK_PREFETCH
+#define QK_PREFETCH 6
+#endif
+
 namespace fa {
 
 // ===================================================== bf16 / fp8 ========
@@ -429,6 +433,18 @@ void fwd_bf16_kernel(FwdParams p) {
         acc = mfma_bf16(a, qr[kb], acc);
       }
       s[kb32] = acc;
+    }
+    // Keep QK_PREFETCH K fragments in flight ahead of the MFMA that uses them,
+    // so LDS latency overlaps the MFMA chain instead of stalling each step.
+    {
+      constexpr int NM = (BC / 32) * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+#pragma unroll
+      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
     }
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
 #pragma unroll
