@@ -537,6 +537,224 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// =================================================== bf16, ping-pong =====
+// Eight waves, two per SIMD.  Waves 0-3 run each tile as QK -> softmax -> PV;
+// waves 4-7 run PV of the previous tile first, then QK -> softmax.  The two
+// waves that share a SIMD are therefore always in different phases, so one
+// wave's softmax (VALU) overlaps the other's products (MFMA) instead of both
+// contending for the same unit between barriers.  The lagging group keeps
+// its P across the barrier, so V lives in three stages (K in two).
+template <int D, int BC_>
+struct PpCfg {
+  static constexpr int NW = 8, NT = NW * 64, BR = NW * 32, BC = BC_;
+  static constexpr int RB = D * 2;
+  static constexpr int TILE = BC * RB;
+  static constexpr int IPW = TILE / 1024 / NW;
+  static constexpr int NKB = BC / 32;
+  static_assert(IPW >= 1, "tile too small for the DMA split");
+};
+
+template <int D, bool CAUSAL, int BC_>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_pp_kernel(FwdParams p) {
+  using C = PpCfg<D, BC_>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, NKB = C::NKB;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2;
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * RB;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+
+  bf16x8 qr[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    bf16x8 x = {};
+    if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
+    qr[kb] = x;
+  }
+  int dma_k[IPW], dma_v[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
+    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
+  }
+  int koff[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  const int s16 = lane & 15, G = lane >> 4;
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
+  int voff[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  const float c = p.scale_log2;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  bf16x8 pk[NKB][2];
+  bool pend = false;
+
+  auto issue = [&](int j, unsigned char* ks, unsigned char* vs) {
+    const int key0 = j * BC;
+    const int bytes = min(N - key0, BC) * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      dma16_buf<0>(rk, dma_k[i], ks + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rv, dma_v[i], vs + (wid * IPW + i) * 1024);
+    }
+  };
+  // S_j -> P_j (packed bf16) with the online softmax; false if the wave sees
+  // none of the tile's keys.
+  auto qk_softmax = [&](int j, const unsigned char* kl) -> bool {
+    const int key0 = j * BC;
+    if (CAUSAL && key0 > q0 + 31) return false;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + koff[kb]);
+        acc = mfma_bf16(a, qr[kb], acc);
+      }
+      s[kb32] = acc;
+    }
+    {
+      constexpr int NM = NKB * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+#pragma unroll
+      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+    }
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+    mx = max_halves(mx);
+    const float m_cand = mx * c;
+    if (__any(m_cand > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    float ts = 0.f;
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m_run));
+          const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m_run));
+          w4[w] = pack_bf16(e0, e1);
+          ts = add_bf16_pair(w4[w], ts);
+        }
+        pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+      }
+    l_run += ts;
+    return true;
+  };
+  auto pv = [&](const unsigned char* vl) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x4 lo = lds_read_tr16(vb + voff[db]);
+          const bf16x4 hi = lds_read_tr16(vb + 8 * RB + voff[db]);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
+        }
+      }
+  };
+  // K_j lives in stage j % 2, V_j in stage j % 3.
+  auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, const unsigned char* vp,
+                  unsigned char* kn, unsigned char* vn) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, kn, vn);
+    if (grp == 1 && pend) pv(vp);
+    pend = qk_softmax(j, kc);
+    if (grp == 0 && pend) {
+      pv(vc);
+      pend = false;
+    }
+  };
+
+  issue(0, k0, v0);
+  for (int j = 0; j < n_tiles; j += 6) {
+    step(j, k0, v0, v2, k1, v1);
+    if (j + 1 < n_tiles) step(j + 1, k1, v1, v0, k0, v2);
+    if (j + 2 < n_tiles) step(j + 2, k0, v2, v1, k1, v0);
+    if (j + 3 < n_tiles) step(j + 3, k1, v0, v2, k0, v1);
+    if (j + 4 < n_tiles) step(j + 4, k0, v1, v0, k1, v2);
+    if (j + 5 < n_tiles) step(j + 5, k1, v2, v1, k0, v0);
+  }
+  if (grp == 1 && pend) {
+    const int r = (n_tiles - 1) % 3;
+    pv(r == 0 ? v0 : (r == 1 ? v1 : v2));
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
 // ========================================================== fp32 ==========
 // fp32 inputs on the fp32 MFMA (32x32x2); probabilities stay fp32.
 template <int D, bool CAUSAL, int NW>
@@ -749,13 +967,17 @@ static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// (waves, keys per tile) per head dim: d = 128 shares 128-key tiles among 8
-// waves (one 128 KB double-buffered stage set per CU); d = 64 and 256 keep
-// 4 waves and 64-key tiles.
+template <int D, bool CAUSAL, int BC>
+static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
+  finish_grid(p, PpCfg<D, BC>::BR);
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC>), dim3(p.total), dim3(PpCfg<D, BC>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
     case 64: return causal ? launch_bf16<64, true, 4, 64>(p, s) : launch_bf16<64, false, 4, 64>(p, s);
-    case 128: return causal ? launch_bf16<128, true, 8, 128>(p, s) : launch_bf16<128, false, 8, 128>(p, s);
+    case 128: return causal ? launch_pp<128, true, 64>(p, s) : launch_pp<128, false, 64>(p, s);
     case 256: return causal ? launch_bf16<256, true, 4, 64>(p, s) : launch_bf16<256, false, 4, 64>(p, s);
   }
   return hipErrorInvalidValue;
