@@ -32,7 +32,7 @@
 #include "fa_kernels.hpp"
 
 #ifndef QK_PREFETCH
-#define QK_PREFETCH 6
+#define QK_PREFETCH 8
 #endif
 
 namespace fa {
@@ -597,14 +597,17 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
     dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
   }
-  int koff[D / 16];
+  // The swizzles touch only the low 4 bits of a 16-byte unit index, so units
+  // 16 apart share one per-lane offset (+256 bytes, an immediate).
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8, NVO = D / 32 < 4 ? D / 32 : 4;
+  int koff[NKO];
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  for (int kb = 0; kb < NKO; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
   const int s16 = lane & 15, G = lane >> 4;
   const int vrow = 4 * (G >> 1) + (s16 >> 2);
-  int voff[D / 32];
+  int voff[NVO];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
 
   const float c = p.scale_log2;
@@ -631,17 +634,17 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   auto qk_softmax = [&](int j, const unsigned char* kl) -> bool {
     const int key0 = j * BC;
     if (CAUSAL && key0 > q0 + 31) return false;
+    // consecutive MFMAs go to different accumulators (no back-to-back chain)
     f32x16 s[NKB];
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32) {
-      f32x16 acc = {};
+    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + koff[kb]);
-        acc = mfma_bf16(a, qr[kb], acc);
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
+        s[kb32] = mfma_bf16(a, qr[kb], s[kb32]);
       }
-      s[kb32] = acc;
-    }
     {
       constexpr int NM = NKB * (D / 16);
       __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
@@ -653,12 +656,14 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
     }
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+      // key = key0 + 4g + rel, rel a compile-time constant per register
+      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
 #pragma unroll
       for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel > lim) s[kb32][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -704,8 +709,9 @@ void fwd_bf16_pp_kernel(FwdParams p) {
         const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo = lds_read_tr16(vb + voff[db]);
-          const bf16x4 hi = lds_read_tr16(vb + 8 * RB + voff[db]);
+          const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+          const bf16x4 lo = lds_read_tr16(vr);
+          const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
           o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
         }
       }
@@ -974,9 +980,15 @@ static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Kernel choice per (head dim, mask), from measurements on MI355X:
+//  * d = 128: ping-pong, 8 waves, 64-key tiles;
+//  * d = 64 non-causal: ping-pong, 128-key tiles;
+//  * d = 64 causal and d = 256: four independent waves per workgroup with
+//    128-row tiles (twice the workgroups of the ping-pong kernel: better
+//    balance for short causal grids; d = 256 does not fit two waves a SIMD).
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_bf16<64, true, 4, 64>(p, s) : launch_bf16<64, false, 4, 64>(p, s);
+    case 64: return causal ? launch_bf16<64, true, 4, 64>(p, s) : launch_pp<64, false, 128>(p, s);
     case 128: return causal ? launch_pp<128, true, 64>(p, s) : launch_pp<128, false, 64>(p, s);
     case 256: return causal ? launch_bf16<256, true, 4, 64>(p, s) : launch_bf16<256, false, 4, 64>(p, s);
   }
