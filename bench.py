@@ -99,6 +99,15 @@ class Case:
                   scale=self.scale, workspace=self.ws, dq=self.dq, dk=self.dk, dv=self.dv)
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def syn_workload(name):
+    import synthetic as syn
+    return syn.WORKLOADS[name]
+
+
 def kernel_name(w, direction="fwd"):
     if direction == "bwd":
         return f"bwd_bf16_d{w.d}_{'causal' if w.causal else 'full'}"
@@ -199,56 +208,70 @@ def main():
         return
 
     names = [args.only] if args.only else STEP
-    cases = [Case(n, dev) for n in names]
-    step_flops = sum(c.w.flops_fwd() for c in cases)
-
-    def step():
-        for c in cases:
-            c.fwd()
+    cases = [Case(n, dev, backward=syn_workload(n).backward and bool(args.only)) for n in names]
+    step_flops = sum(c.w.flops_fwd() + (c.w.flops_bwd() if c.backward else 0.0) for c in cases)
+    log(f"timing {args.steps} steps of {names} after {args.warmup} warm-up steps")
 
     for _ in range(args.warmup):
-        step()
+        for c in cases:
+            c.fwd()
+            if c.backward:
+                c.bwd()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    per = {c.w.name: [] for c in cases}
+    per = {}          # (workload, direction) -> per-launch ms
     ev = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(st)
     for _ in range(args.steps):
         for c in cases:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(st)
-            c.fwd()
-            b.record(st)
-            ev.append((c.w.name, a, b))
+            for direction, fn in (("fwd", c.fwd), ("bwd", c.bwd)):
+                if direction == "bwd" and not c.backward:
+                    continue
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                fn()
+                b.record(st)
+                ev.append(((c.w.name, direction), a, b))
     t_end.record(st)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    for name, a, b in ev:
-        per[name].append(a.elapsed_time(b))
+    for key, a, b in ev:
+        per.setdefault(key, []).append(a.elapsed_time(b))
     ms_per_step = total_ms / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"{ms_per_step:.4f} ms per step, {value:.1f} TFLOP/s")
 
-    # dominant kernel: most time inside the timed region
-    dom = max(cases, key=lambda c: sum(per[c.w.name]))
-    dom_ms = sum(per[dom.w.name]) / len(per[dom.w.name])
+    # dominant kernel: the forward launch with the most time inside the timed region
+    by_name = {c.w.name: c for c in cases}
+    fwd_keys = [k for k in per if k[1] == "fwd"]
+    dom_key = max(fwd_keys, key=lambda k: sum(per[k]))
+    dom = by_name[dom_key[0]]
+    dom_ms = sum(per[dom_key]) / len(per[dom_key])
     achieved = dom.w.flops_fwd() / (dom_ms * 1e-3) / 1e12
-    traffic = load_traffic().get(kernel_name(dom.w))
+    tr = load_traffic().get(kernel_name(dom.w))
+    traffic = tr["bytes_per_launch"] if tr else None
     roofline = {"bound": "mfma", "kernel": kernel_name(dom.w), "workload": dom.w.name,
                 "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dom.w.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom.w.dtype], 4),
                 "avg_launch_ms": round(dom_ms, 4),
-                "traffic": traffic}
-    cases_out = {c.w.name: {"ms_median": round(median(per[c.w.name]), 4),
-                            "tflops": round(c.w.flops_fwd() / (median(per[c.w.name]) * 1e-3) / 1e12, 2)}
-                 for c in cases}
+                "traffic": traffic,
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_detail": tr}
+    cases_out = {}
+    for (name, direction), xs in per.items():
+        w = by_name[name].w
+        fl = w.flops_fwd() if direction == "fwd" else w.flops_bwd()
+        cases_out[f"{name}.{direction}"] = {"ms_median": round(median(xs), 4),
+                                            "tflops": round(fl / (median(xs) * 1e-3) / 1e12, 2)}
 
     extra = {}
     if not args.no_extra and not args.only:
         del cases
         torch.cuda.empty_cache()
         for name in EXTRA_FWD:
+            log(f"extra: {name}")
             c = Case(name, dev)
             ms = median(time_launches(c.fwd, reps=10, warmup=2))
             tf = c.w.flops_fwd() / (ms * 1e-3) / 1e12
@@ -256,6 +279,7 @@ def main():
                            "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
             del c
             torch.cuda.empty_cache()
+        log("extra: C4 forward + backward")
         c = Case("C4", dev, backward=True)
         ms_f = median(time_launches(c.fwd, reps=10, warmup=2))
         ms_b = median(time_launches(c.bwd, reps=10, warmup=2))
@@ -271,6 +295,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not args.only:
+        log("cpu baseline (oracle)")
         cpu = cpu_baseline()
 
     out = {
@@ -284,7 +309,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": cases[0].w.dtype if args.only else "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, bf16 RNE)",
         "config": {"workload": "bf16 forward: B=1,H=8,N=8192,d=64 causal + non-causal; "
                                "B=8,H=16,N=2048,d=256 causal" if not args.only else args.only,
