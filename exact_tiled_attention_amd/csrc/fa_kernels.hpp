@@ -33,6 +33,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;        // workspace: rowsum(dO * O), [B][H][N]
+  float* lse2;         // workspace: LSE * log2(e), [B][H][N]
   int B, H, H_kv, N;
   int n_tiles;         // tiles per head of the kernel being launched
   int total;

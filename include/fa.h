@@ -88,7 +88,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
 
 /*
  * Bytes of device workspace fa_bwd needs for this problem (0 on invalid
- * arguments).  The workspace holds D = rowsum(dO * O) in fp32.
+ * arguments).  The workspace holds two fp32 [B][H][N] arrays: D = rowsum(dO * O)
+ * and the forward's LSE in base-2 units.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dtype);
 

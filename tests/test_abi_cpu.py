@@ -71,7 +71,7 @@ def fwd(lib, q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, qs=None, ks=None, vs=Non
     return lib.fa_fwd(q, k, v, o, lse, qs, ks, vs, B, H, Hkv, N, d, scale, causal, dtype, None)
 
 
-def bwd(lib, ws=64 * P, ws_bytes=1 << 20, d=64, dtype=1, N=16, H=2, Hkv=2, B=1, scale=0.125,
+def bwd(lib, ws=64 * P, ws_bytes=1 << 21, d=64, dtype=1, N=16, H=2, Hkv=2, B=1, scale=0.125,
         ptrs=None):
     p = ptrs or [P * (i + 1) for i in range(9)]
     return lib.fa_bwd(*p, ws, ws_bytes, B, H, Hkv, N, d, scale, 1, dtype, None)
@@ -110,6 +110,6 @@ def test_bwd_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    assert fa.fa_bwd_workspace_bytes(2, 16, 16, 16384, 64) == 2 * 16 * 16384 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(2, 16, 16, 16384, 64) == 2 * (2 * 16 * 16384 * 4)
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 512
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 3, 64) == 0
