@@ -31,6 +31,9 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
+#ifndef PV_PREFETCH
+#define PV_PREFETCH 8
+#endif
 #ifndef QK_PREFETCH
 #define QK_PREFETCH 8
 #endif
@@ -718,6 +721,18 @@ void fwd_bf16_pp_kernel(FwdParams p) {
           o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
         }
       }
+    // V fragments run PV_PREFETCH reads (two per MFMA) ahead of their MFMA.
+    {
+      constexpr int NM = NKB * 2 * (D / 32);
+      constexpr int PF = PV_PREFETCH < 2 * NM ? PV_PREFETCH : 2 * NM;
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int i = 0; i < NM - PF / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, PF / 2, 0);
+    }
   };
   // K_j lives in stage j % 2, V_j in stage j % 3.
   auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, const unsigned char* vp,
