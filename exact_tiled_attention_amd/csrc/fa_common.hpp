@@ -23,6 +23,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // this many powers of two, so most tiles skip the rescale of the output;
 // probabilities then stay below 2^kRescaleSlack, far inside fp32/bf16 range.
 constexpr float kRescaleSlack = 8.0f;
+// Bound on one lane's partial row sum of a tile's probabilities taken against
+// a stale running max (each term is then at most 2^12).
+constexpr float kSumBound = 4096.0f;
 
 // ---------------------------------------------------------------- MFMA ----
 // 32x32 output tile, fp32 accumulate.  Output layout (all 32x32 shapes):

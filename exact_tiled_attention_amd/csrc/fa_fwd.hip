@@ -19,9 +19,14 @@
 // Online softmax ("FlashAttentionとは？…", 最大値と正規化項を持ち回るオンライン
 // softmaxの再スケール): running max m and running sum l per row; exp2 with
 // scale*log2(e) folded into one FMA; 1/l applied once in the epilogue.  The
-// rescale of the accumulator is skipped unless a tile's max exceeds m by more
-// than kRescaleSlack (a wave-uniform test), which keeps the result exact up
-// to rounding because m only has to bound the scores, not equal their max.
+// result is exact up to rounding for any m, as long as numerator and
+// denominator use the same one and exp2(score - m) stays in range, so m is
+// moved (and the accumulator rescaled) only when needed.  The fp8 and fp32
+// kernels take each tile's max and move m when it exceeds m by more than
+// kRescaleSlack; the bf16 kernels do not even take the max: they form P
+// against the current m and fall back to the max-and-rescale path only when
+// a lane's partial row sum leaves [0, kSumBound] (a wave-uniform test that
+// also catches the first tile, where m is still -inf).
 //
 // Causal: key tiles past the work-group's last query are never loaded; the
 // mask is applied only on tiles that straddle the diagonal or the sequence
@@ -461,15 +466,39 @@ void fwd_bf16_kernel(FwdParams p) {
           if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P against the running max first; the tile max is only taken when some
+    // lane's partial row sum leaves [0, kSumBound]: a score far above the
+    // running max, or the first tile of the rows (running max still -inf).
+    // P is rounded to bf16 (the PV operand) and the row sum is taken from the
+    // same rounded values, two at a time, so numerator and denominator agree.
+    bf16x8 pk[BC / 32][2];
+    auto expo = [&](float m) -> float {
+      float t = 0.f;
 #pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-    mx = max_halves(mx);
-    const float m_cand = mx * c;
-    if (__any(m_cand > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, m_cand);
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
+            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
+            w4[w] = pack_bf16(e0, e1);
+            t = add_bf16_pair(w4[w], t);
+          }
+          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+      return t;
+    };
+    float ts = expo(m_run);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -477,25 +506,8 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ts = expo(m_run);
     }
-    // P in bf16 (the PV operand); the row sum is taken from the same rounded
-    // values, two at a time, so numerator and denominator use one P.
-    float ts = 0.f;
-    bf16x8 pk[BC / 32][2];
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m_run));
-          const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m_run));
-          w4[w] = pack_bf16(e0, e1);
-          ts = add_bf16_pair(w4[w], ts);
-        }
-        pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
-      }
     l_run += ts;
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32)
@@ -672,15 +684,36 @@ void fwd_bf16_pp_kernel(FwdParams p) {
           if (rel > lim) s[kb32][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P against the running max first; the tile max is only taken when some
+    // lane's partial row sum leaves [0, kSumBound]: a score far above the
+    // running max, or the first tile of the rows (running max still -inf).
+    auto expo = [&](float m) -> float {
+      float t = 0.f;
 #pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32)
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-    mx = max_halves(mx);
-    const float m_cand = mx * c;
-    if (__any(m_cand > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, m_cand);
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
+            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
+            w4[w] = pack_bf16(e0, e1);
+            t = add_bf16_pair(w4[w], t);
+          }
+          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+      return t;
+    };
+    float ts = expo(m_run);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -688,22 +721,8 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ts = expo(m_run);
     }
-    float ts = 0.f;
-#pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m_run));
-          const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m_run));
-          w4[w] = pack_bf16(e0, e1);
-          ts = add_bf16_pair(w4[w], ts);
-        }
-        pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
-      }
     l_run += ts;
     return true;
   };
