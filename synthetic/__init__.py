@@ -130,20 +130,29 @@ def make_inputs(w: Workload, with_do: bool | None = None):
     if with_do is None:
         with_do = w.backward
     q, k, v, do = draw(w.B, w.H, w.H_kv, w.N, w.d, w.amp, w.seed, with_do)
+    return pack_inputs(q, k, v, do, w.dtype)
+
+
+def pack_inputs(q, k, v, do, dtype: str):
+    """Cast fp32 CPU tensors ``q, k, v`` (and ``do`` or None) to a kernel dtype.
+
+    Returns the dict described under make_inputs; the softmax scale is
+    1/sqrt(d) for the head dim of ``q``.
+    """
     out = {"q_scale": None, "k_scale": None, "v_scale": None, "do": None, "do_64": None}
-    if w.dtype == "f32":
+    if dtype == "f32":
         out.update(q=q, k=k, v=v)
         if do is not None:
             out["do"] = do
         exact = (q.double(), k.double(), v.double(), do.double() if do is not None else None)
-    elif w.dtype == "bf16":
+    elif dtype == "bf16":
         qb, kb, vb = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
         out.update(q=qb, k=kb, v=vb)
         if do is not None:
             out["do"] = do.to(torch.bfloat16)
         exact = (qb.double(), kb.double(), vb.double(),
                  out["do"].double() if do is not None else None)
-    elif w.dtype == "fp8":
+    elif dtype == "fp8":
         (qc, qs), (kc, ks), (vc, vs) = (quantize_fp8_blocks(t) for t in (q, k, v))
         out.update(q=qc, k=kc, v=vc, q_scale=qs, k_scale=ks, v_scale=vs)
         exact = (dequantize_fp8_blocks_torch(qc, qs), dequantize_fp8_blocks_torch(kc, ks),
@@ -151,11 +160,11 @@ def make_inputs(w: Workload, with_do: bool | None = None):
         if do is not None:
             out["do"] = do.to(torch.bfloat16)
     else:
-        raise ValueError(f"unknown dtype {w.dtype!r}")
+        raise ValueError(f"unknown dtype {dtype!r}")
     out["q_64"], out["k_64"], out["v_64"] = (t.numpy() for t in exact[:3])
     if exact[3] is not None:
         out["do_64"] = exact[3].numpy()
-    out["scale"] = 1.0 / math.sqrt(w.d)
+    out["scale"] = 1.0 / math.sqrt(q.shape[-1])
     return out
 
 
