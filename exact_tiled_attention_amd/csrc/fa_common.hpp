@@ -131,6 +131,15 @@ __device__ __forceinline__ int rt_swz(int row, int u) {
                    : (u ^ (((row & 1) << 3) | ((row & 2) << 1) | ((row >> 2) & 3)));
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier for LDS stages: each wave's own LDS reads and writes
+// complete first, but its global loads (LDS-DMA prefetches of later tiles,
+// waited for separately by count) stay in flight.  A memory fence would make
+// the compiler wait for every LDS-DMA write as well, so the barrier is a bare
+// s_barrier whose "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

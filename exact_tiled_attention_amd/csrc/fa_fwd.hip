@@ -39,6 +39,18 @@
 #ifndef PV_PREFETCH
 #define PV_PREFETCH 8
 #endif
+#ifndef FA_NST64
+#define FA_NST64 2
+#endif
+#ifndef FA_BC256
+#define FA_BC256 64
+#endif
+#ifndef FA_NST256
+#define FA_NST256 2
+#endif
+#ifndef FA_D256_PAIRS
+#define FA_D256_PAIRS 1
+#endif
 #ifndef QK_PREFETCH
 #define QK_PREFETCH 8
 #endif
@@ -334,14 +346,23 @@ void fwd_mfma_kernel(FwdParams p) {
 // bank conflicts.  The two stages live in two distinct LDS arrays and the
 // tile loop is unrolled by two, so the compiler can see that the prefetch into
 // one stage never aliases the reads from the other.
-template <int D, int NW_, int BC_>
+template <int D, int NW_, int BC_, int NST_>
 struct Bf16Cfg {
-  static constexpr int NW = NW_, NT = NW * 64, BR = NW * 32, BC = BC_;
+  static constexpr int NW = NW_, NT = NW * 64, BR = NW * 32, BC = BC_, NST = NST_;
   static constexpr int RB = D * 2;              // bytes per K/V row in LDS
   static constexpr int TILE = BC * RB;          // bytes per K (or V) tile
   static constexpr int IPW = TILE / 1024 / NW;  // 1 KB DMA issues per wave per tensor
   static_assert(IPW >= 1, "tile too small for the DMA split");
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  static_assert(2 * IPW * (NST - 2) < 64, "DMA count must fit the vmcnt field");
 };
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order), N a compile-time constant < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
+}
 // XOR swizzles of the 16-byte units of a K or V row in LDS (the DMA writes
 // rows unpadded).  They were chosen by measuring the operand reads on MI355X
 // (rocprof-free microbenchmarks of the exact access patterns):
@@ -360,13 +381,15 @@ __device__ __forceinline__ int v_swz(int row, int u) {
   return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ (((row & 1) << 3) | ((row & 2) << 1)));
 }
 
-template <int D, bool CAUSAL, int NW, int BC_>
+template <int D, bool CAUSAL, int NW, int BC_, int NST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
-  using C = Bf16Cfg<D, NW, BC_>;
+  using C = Bf16Cfg<D, NW, BC_, NST>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[NST > 2 ? 2 * C::TILE : 1];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[NST > 3 ? 2 * C::TILE : 1];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -402,14 +425,17 @@ void fwd_bf16_kernel(FwdParams p) {
     dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;   // the swizzle is an involution
     dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
   }
-  int koff[D / 16];
+  // The swizzles touch only the low 4 bits of a 16-byte unit index, so units
+  // 16 apart share one per-lane offset (+256 bytes, an immediate).
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8, NVO = D / 32 < 4 ? D / 32 : 4;
+  int koff[NKO];
 #pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  for (int kb = 0; kb < NKO; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
   const int s16 = lane & 15, G = lane >> 4;
   const int vrow = 4 * (G >> 1) + (s16 >> 2);
-  int voff[D / 32];
+  int voff[NVO];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
 
   const float c = p.scale_log2;
@@ -440,7 +466,7 @@ void fwd_bf16_kernel(FwdParams p) {
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + koff[kb]);
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
         acc = mfma_bf16(a, qr[kb], acc);
       }
       s[kb32] = acc;
@@ -517,24 +543,38 @@ void fwd_bf16_kernel(FwdParams p) {
         const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo = lds_read_tr16(vb + voff[db]);
-          const bf16x4 hi = lds_read_tr16(vb + 8 * RB + voff[db]);
+          const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+          const bf16x4 lo = lds_read_tr16(vr);
+          const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
           o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[db]);
         }
       }
   };
 
-  issue(0, stage0);
-  for (int j = 0; j < n_tiles; j += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < n_tiles) issue(j + 1, stage1);
-    consume(j, stage0);
-    if (j + 1 < n_tiles) {
-      wait_vmem();
-      __syncthreads();
-      if (j + 2 < n_tiles) issue(j + 2, stage0);
-      consume(j + 1, stage1);
+  // Tile j lives in stage j % NST and is loaded NST - 1 tiles ahead.  Before
+  // tile j is read, each wave waits for its own DMA of that tile (the later
+  // tiles' DMAs, issued after it, may stay in flight) and the barrier makes
+  // every wave's part visible; the same barrier retires the stage that the
+  // next prefetch overwrites (tile j - 1's).
+  auto stage = [&](int u) -> unsigned char* {
+    return u == 0 ? stage0 : (u == 1 ? stage1 : (u == 2 ? stage2 : stage3));
+  };
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u)
+    if (u < n_tiles) issue(u, stage(u));
+  for (int j0 = 0; j0 < n_tiles; j0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int j = j0 + u;
+      if (j < n_tiles) {
+        const int later = min(NST - 2, n_tiles - 1 - j);   // tiles issued after j
+        if (NST > 3 && later >= 2) wait_vmem_upto<2 * 2 * IPW>();
+        else if (NST > 2 && later >= 1) wait_vmem_upto<2 * IPW>();
+        else wait_vmem();
+        barrier_lds();
+        if (j + NST - 1 < n_tiles) issue(j + NST - 1, stage((u + NST - 1) % NST));
+        consume(j, stage(u));
+      }
     }
   }
 
@@ -798,6 +838,286 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   }
 }
 
+// ====================================================== bf16, d = 256 =====
+// Head dim 256: a 32-row block of O alone takes 128 fp32 registers a lane, so
+// one wave per 32 rows cannot run two waves a SIMD.  Here the two waves that
+// share a SIMD (w and w + 4) own the same 32 rows and split O by columns
+// (role r holds columns 128r .. 128r + 127).  Key tiles alternate between
+// them: the owner of tile t (role t & 1) computes S_t = K_t Q^T over the whole
+// head dim and the softmax, and publishes P_t (bf16), the max it used and the
+// row sums through LDS; both waves then add P_t V_t into their half of O.
+// One phase per tile, between workgroup barriers:
+//   owner of t:  P_{t-1} from LDS -> O += P_{t-1} V_{t-1};  softmax of S_t -> LDS
+//   the other:   O += P_{t-1} V_{t-1} (its own P);          S_{t+1} = K_{t+1} Q^T
+// so on each SIMD one wave's softmax (VALU) runs under the other's products.
+// The running max is shared: P_t is formed against the max published with
+// P_{t-1} (moved only on the slow path), and before adding P_t V_t each wave
+// rescales its half of O (and the row sum) to P_t's max, so both halves and
+// both copies of the row sum follow the same sequence of maxima exactly.
+template <int D>
+struct PairCfg {
+  static constexpr int NW = 8, NT = 512, NPAIR = 4, BR = NPAIR * 32, BC = 64;
+  static constexpr int RB = D * 2;               // bytes per K/V row
+  static constexpr int TILE = BC * RB;           // one K (or V) tile
+  static constexpr int IPW = TILE / 1024 / NW;   // 1 KB DMA issues per wave per tensor
+  static constexpr int DH = D / 2;               // columns of O per wave
+  static constexpr int PBYTES = 2 * 2 * 64 * 16; // one P tile of a pair (B-operand fragments)
+  static_assert(IPW >= 1, "tile too small for the DMA split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_pairs_kernel(FwdParams p) {
+  using C = PairCfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, DH = C::DH;
+  constexpr int NKB = BC / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char pbuf[C::NPAIR * C::PBYTES];
+  __shared__ float mbuf[C::NPAIR * 64];
+  __shared__ float sbuf[C::NPAIR * 64];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wid & 3, role = wid >> 2;
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * RB;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + pr * 32;              // first row of the pair
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  // tiles the pair takes part in: 0 .. t_end - 1
+  const int t_end = CAUSAL ? min(n_tiles, (q0 + 31) / BC + 1) : n_tiles;
+
+  bf16x8 qr[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    bf16x8 x = {};
+    if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
+    qr[kb] = x;
+  }
+  int dma_k[IPW], dma_v[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
+    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
+  }
+  // The swizzles touch only the low 4 bits of a 16-byte unit index, so units
+  // 16 apart share one per-lane offset (+256 bytes, an immediate).
+  constexpr int NKO = 8, NVO = DH / 32;
+  static_assert(DH == 128, "the column split assumes 16 units of 16 bytes per half row");
+  int koff[NKO];
+#pragma unroll
+  for (int kb = 0; kb < NKO; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  const int s16 = lane & 15, G = lane >> 4;
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
+  int voff[NVO];   // this wave's half of the columns starts 16 units (256 bytes) in for role 1
+#pragma unroll
+  for (int db = 0; db < NVO; ++db)
+    voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8 +
+               role * 256;
+
+  const float c = p.scale_log2;
+  f32x16 o[DH / 32];
+#pragma unroll
+  for (int i = 0; i < DH / 32; ++i) o[i] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;   // the max O and l are scaled to
+  float m_own = -INFINITY, ts_own = 0.f;  // stats of the last tile this wave owned
+  f32x16 s[NKB];
+  bf16x8 pk[NKB][2];
+  unsigned char* pb = pbuf + pr * C::PBYTES + lane * 16;
+  float* mb = mbuf + pr * 64 + lane;
+  float* sb = sbuf + pr * 64 + lane;
+
+  auto issue = [&](const unsigned char* src, const int* off, int t, unsigned char* st) {
+    const int key0 = t * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
+  };
+  auto qk = [&](const unsigned char* kl) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
+        s[kb32] = mfma_bf16(a, qr[kb], s[kb32]);
+      }
+    {
+      constexpr int NM = NKB * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+#pragma unroll
+      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+    }
+  };
+  // Bring O and l to the max of the tile about to be added, then add its sums.
+  auto rebase = [&](float m_t, float ts_t) {
+    if (__any(m_t > m_ref)) {
+      const float m_new = fmaxf(m_ref, m_t);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DH / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+    l_run += ts_t;
+  };
+  // O += P V for this wave's columns; P fragments from registers or LDS.
+  auto pv = [&](const unsigned char* vl, bool from_lds) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 pf = from_lds ? *(const bf16x8*)(pb + (kb32 * 2 + half) * 1024) : pk[kb32][half];
+        const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+        for (int db = 0; db < DH / 32; ++db) {
+          const unsigned char* vr = vb + voff[db];
+          const bf16x4 lo = lds_read_tr16(vr);
+          const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf, o[db]);
+        }
+      }
+  };
+  // Softmax of S_t against m_prev; leaves P_t in pk and publishes it.
+  auto softmax = [&](int t, float m_prev) {
+    const int key0 = t * BC;
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel > lim) s[kb32][r] = -INFINITY;
+        }
+    }
+    auto expo = [&](float m) -> float {
+      float acc = 0.f;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
+            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
+            w4[w] = pack_bf16(e0, e1);
+            acc = add_bf16_pair(w4[w], acc);
+          }
+          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+      return acc;
+    };
+    float m = m_prev;
+    float ts = expo(m);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = max_halves(mx);
+      m = fmaxf(m, mx * c);
+      ts = expo(m);
+    }
+    m_own = m;
+    ts_own = sum_halves(ts);
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) *(bf16x8*)(pb + (kb32 * 2 + half) * 1024) = pk[kb32][half];
+    *mb = m_own;
+    *sb = ts_own;
+  };
+
+  // Phase ph: K_{ph+1} and V_{ph-1} are read; K_{ph+2} and V_ph are loaded.
+  // K_t lives in stage t & 1 of k, V_t in stage t & 1 of v.  Role 0 owns the
+  // even tiles, role 1 the odd ones; each role runs its own copy of the loop
+  // (same barriers, same order), so the compiler sees which values live
+  // across a phase: P after an owner phase, S after the other one.
+  auto begin = [&](int ph, unsigned char* k_load, unsigned char* v_load) {
+    wait_vmem();
+    __syncthreads();
+    if (ph + 2 < n_tiles) issue(kg, dma_k, ph + 2, k_load);
+    if (ph >= 0 && ph < n_tiles) issue(vg, dma_v, ph, v_load);
+  };
+  auto as_owner = [&](int ph, const unsigned char* v_use) {
+    // the partner's tile ph - 1: its max, row sums and P come from LDS
+    const float m_prev = ph >= 1 ? *mb : -INFINITY;
+    if (ph >= 1 && ph - 1 < t_end) {
+      rebase(m_prev, *sb);
+      pv(v_use, true);
+    }
+    if (ph >= 0 && ph < t_end) softmax(ph, m_prev);
+  };
+  auto as_other = [&](int ph, const unsigned char* k_use, const unsigned char* v_use) {
+    if (ph >= 1 && ph - 1 < t_end) {
+      rebase(m_own, ts_own);
+      pv(v_use, false);
+    }
+    if (ph + 1 < t_end) qk(k_use);
+  };
+
+  issue(kg, dma_k, 0, k0);
+  if (role == 0) {
+    for (int ph = -1; ph <= n_tiles; ph += 2) {
+      begin(ph, k1, v1);                  // ph odd: K_{ph+1} in k0, V_{ph-1} in v0
+      as_other(ph, k0, v0);
+      if (ph + 1 <= n_tiles) {
+        begin(ph + 1, k0, v0);            // ph + 1 even: K in k1, V in v1
+        as_owner(ph + 1, v1);
+      }
+    }
+  } else {
+    for (int ph = -1; ph <= n_tiles; ph += 2) {
+      begin(ph, k1, v1);
+      as_owner(ph, v0);
+      if (ph + 1 <= n_tiles) {
+        begin(ph + 1, k0, v0);
+        as_other(ph + 1, k1, v1);
+      }
+    }
+  }
+
+  // l_run already holds whole-row sums (the published sums were combined
+  // across the two halves of the wave).
+  if (myq < N) {
+    const float inv = 1.f / l_run;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D + role * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0 && role == 0) p.lse[(size_t)wi.bh * N + myq] = (m_ref + fast_log2(l_run)) * kLn2;
+  }
+}
+
 // ========================================================== fp32 ==========
 // fp32 inputs on the fp32 MFMA (32x32x2); probabilities stay fp32.
 template <int D, bool CAUSAL, int NW>
@@ -1002,11 +1322,18 @@ static hipError_t launch_mfma(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int NW, int BC>
+template <int D, bool CAUSAL, int NW, int BC, int NST>
 static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
-  using C = Bf16Cfg<D, NW, BC>;
+  using C = Bf16Cfg<D, NW, BC, NST>;
   finish_grid(p, C::BR);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC>), dim3(p.total), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST>), dim3(p.total), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
+  finish_grid(p, PairCfg<D>::BR);
+  hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1025,9 +1352,14 @@ static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
 //    balance for short causal grids; d = 256 does not fit two waves a SIMD).
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_bf16<64, true, 4, 64>(p, s) : launch_pp<64, false, 128>(p, s);
+    case 64: return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128>(p, s);
     case 128: return causal ? launch_pp<128, true, 64>(p, s) : launch_pp<128, false, 64>(p, s);
-    case 256: return causal ? launch_bf16<256, true, 4, 64>(p, s) : launch_bf16<256, false, 4, 64>(p, s);
+#if FA_D256_PAIRS
+    case 256: return causal ? launch_pairs<256, true>(p, s) : launch_pairs<256, false>(p, s);
+#else
+    case 256: return causal ? launch_bf16<256, true, 4, FA_BC256, FA_NST256>(p, s)
+                            : launch_bf16<256, false, 4, FA_BC256, FA_NST256>(p, s);
+#endif
   }
   return hipErrorInvalidValue;
 }
