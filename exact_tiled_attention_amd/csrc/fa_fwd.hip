@@ -51,6 +51,12 @@
 #ifndef FA_D256_PAIRS
 #define FA_D256_PAIRS 1
 #endif
+#ifndef FA_SUM_F32
+#define FA_SUM_F32 1
+#endif
+#ifndef FA_PP2
+#define FA_PP2 1
+#endif
 #ifndef QK_PREFETCH
 #define QK_PREFETCH 8
 #endif
@@ -510,7 +516,11 @@ void fwd_bf16_kernel(FwdParams p) {
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
+#if FA_SUM_F32
+            t += e0 + e1;
+#else
             t = add_bf16_pair(w4[w], t);
+#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
@@ -621,7 +631,9 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILE];
+#if !FA_PP2
   __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILE];
+#endif
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -687,6 +699,100 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       dma16_buf<0>(rv, dma_v[i], vs + (wid * IPW + i) * 1024);
     }
   };
+  auto issue_one = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
+    const int key0 = j * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
+  };
+#if FA_PP2
+  // S_j = K_j Q^T into s (false if the wave sees none of the tile's keys), and
+  // the online softmax of S_j into P_j (packed bf16).
+  f32x16 s[NKB];
+  auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {
+    const int key0 = j * BC;
+    if (CAUSAL && key0 > q0 + 31) return false;
+    // consecutive MFMAs go to different accumulators (no back-to-back chain)
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
+        s[kb32] = mfma_bf16(a, qr[kb], s[kb32]);
+      }
+    {
+      constexpr int NM = NKB * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+#pragma unroll
+      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+    }
+    return true;
+  };
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int key0 = j * BC;
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+      // key = key0 + 4g + rel, rel a compile-time constant per register
+      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel > lim) s[kb32][r] = -INFINITY;
+        }
+    }
+    // P against the running max first; the tile max is only taken when some
+    // lane's partial row sum leaves [0, kSumBound]: a score far above the
+    // running max, or the first tile of the rows (running max still -inf).
+    auto expo = [&](float m) -> float {
+      float t = 0.f;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
+            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
+            w4[w] = pack_bf16(e0, e1);
+#if FA_SUM_F32
+            t += e0 + e1;
+#else
+            t = add_bf16_pair(w4[w], t);
+#endif
+          }
+          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+      return t;
+    };
+    float ts = expo(m_run);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ts = expo(m_run);
+    }
+    l_run += ts;
+  };
+#else
   // S_j -> P_j (packed bf16) with the online softmax; false if the wave sees
   // none of the tile's keys.
   auto qk_softmax = [&](int j, const unsigned char* kl) -> bool {
@@ -739,7 +845,11 @@ void fwd_bf16_pp_kernel(FwdParams p) {
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
+#if FA_SUM_F32
+            t += e0 + e1;
+#else
             t = add_bf16_pair(w4[w], t);
+#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
@@ -766,6 +876,7 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     l_run += ts;
     return true;
   };
+#endif
   auto pv = [&](const unsigned char* vl) {
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32)
@@ -793,6 +904,38 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, PF / 2, 0);
     }
   };
+#if FA_PP2
+  // Phase j: both groups add P_{j-1} V_{j-1} and form S_j = K_j Q^T (32
+  // products); group 0 then runs the softmax of S_j, group 1 ran the softmax
+  // of S_{j-1} first.  So on each SIMD one wave's softmax (VALU) always runs
+  // under the other wave's 32 products.  K_j lives in stage j % 2, V_j in
+  // stage j % 2; phase j loads K_{j+1} and V_j.
+  bool has_s = false, has_p = false;
+  auto step = [&](int j, const unsigned char* kc, const unsigned char* vp, unsigned char* kn,
+                  unsigned char* vn) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_one(kg, dma_k, j + 1, kn);
+    if (j < n_tiles) issue_one(vg, dma_v, j, vn);
+    if (grp == 1 && has_s) {
+      softmax(j - 1);
+      has_p = true;
+    }
+    if (has_p) pv(vp);
+    has_p = false;
+    has_s = j < n_tiles && qk(j, kc);
+    if (grp == 0 && has_s) {
+      softmax(j);
+      has_p = true;
+      has_s = false;
+    }
+  };
+  issue_one(kg, dma_k, 0, k0);
+  for (int j = 0; j <= n_tiles; j += 2) {
+    step(j, k0, v1, k1, v0);
+    if (j + 1 <= n_tiles) step(j + 1, k1, v0, k0, v1);
+  }
+#else
   // K_j lives in stage j % 2, V_j in stage j % 3.
   auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, const unsigned char* vp,
                   unsigned char* kn, unsigned char* vn) {
@@ -821,6 +964,7 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     pv(r == 0 ? v0 : (r == 1 ? v1 : v2));
   }
 
+#endif
   const float l_tot = sum_halves(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -1023,7 +1167,11 @@ void fwd_bf16_pairs_kernel(FwdParams p) {
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
+#if FA_SUM_F32
+            acc += e0 + e1;
+#else
             acc = add_bf16_pair(w4[w], acc);
+#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
