@@ -54,9 +54,6 @@
 #ifndef FA_SUM_F32
 #define FA_SUM_F32 1
 #endif
-#ifndef FA_PP2
-#define FA_PP2 1
-#endif
 #ifndef QK_PREFETCH
 #define QK_PREFETCH 8
 #endif
@@ -606,34 +603,43 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 // =================================================== bf16, ping-pong =====
-// Eight waves, two per SIMD.  Waves 0-3 run each tile as QK -> softmax -> PV;
-// waves 4-7 run PV of the previous tile first, then QK -> softmax.  The two
-// waves that share a SIMD are therefore always in different phases, so one
-// wave's softmax (VALU) overlaps the other's products (MFMA) instead of both
-// contending for the same unit between barriers.  The lagging group keeps
-// its P across the barrier, so V lives in three stages (K in two).
-template <int D, int BC_>
+// Eight waves, two per SIMD (waves w and w + 4 share one).  In phase j every
+// wave adds P_{j-1} V_{j-1} and forms S_j = K_j Q^T (32 products); group 0
+// (waves 0-3) then runs the softmax of S_j, while group 1 ran the softmax of
+// S_{j-1} at the start of the phase.  So on each SIMD one wave's softmax
+// (VALU) always runs under the other wave's products.
+//
+// K and V tiles reach LDS by DMA.  Issuing a DMA can stall a wave for
+// hundreds of cycles when the whole CU issues at once.  With LATE, only group
+// 0 issues, at the end of its phase, where it would otherwise wait at the
+// barrier; tiles then load two phases ahead and K and V each take three
+// stages.  Otherwise every wave issues its share at the start of the phase,
+// one phase ahead, with two stages each.  (Measured: LATE wins for d = 64,
+// where the softmax dominates the phase, and loses for d = 128.)
+template <int D, int BC_, bool LATE>
 struct PpCfg {
   static constexpr int NW = 8, NT = NW * 64, BR = NW * 32, BC = BC_;
   static constexpr int RB = D * 2;
   static constexpr int TILE = BC * RB;
-  static constexpr int IPW = TILE / 1024 / NW;
+  static constexpr int NST = LATE ? 3 : 2;                  // stages per tensor
+  static constexpr int DW = LATE ? 4 : 8;                   // waves that issue DMA
+  static constexpr int IPD = TILE / 1024 / DW;              // 1 KB issues per such wave per tensor
   static constexpr int NKB = BC / 32;
-  static_assert(IPW >= 1, "tile too small for the DMA split");
+  static_assert(IPD >= 1, "tile too small for the DMA split");
+  static_assert(2 * IPD < 64, "DMA count must fit the vmcnt field");
 };
 
-template <int D, bool CAUSAL, int BC_>
+template <int D, bool CAUSAL, int BC_, bool LATE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pp_kernel(FwdParams p) {
-  using C = PpCfg<D, BC_>;
-  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, NKB = C::NKB;
+  using C = PpCfg<D, BC_, LATE>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPD = C::IPD, NKB = C::NKB, NST = C::NST;
   __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2[NST > 2 ? C::TILE : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILE];
-#if !FA_PP2
-  __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILE];
-#endif
+  __shared__ __attribute__((aligned(1024))) unsigned char v2[NST > 2 ? C::TILE : 1];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -659,10 +665,11 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
     qr[kb] = x;
   }
-  int dma_k[IPW], dma_v[IPW];
+  const int dwid = wid & (C::DW - 1);   // this wave's share of a DMA'd tile
+  int dma_k[IPD], dma_v[IPD];
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+  for (int i = 0; i < IPD; ++i) {
+    const int byte = (dwid * IPD + i) * 1024 + lane * 16;
     const int row = byte / RB, pu = (byte % RB) / 16;
     dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
     dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
@@ -686,26 +693,13 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   bf16x8 pk[NKB][2];
-  bool pend = false;
 
-  auto issue = [&](int j, unsigned char* ks, unsigned char* vs) {
-    const int key0 = j * BC;
-    const int bytes = min(N - key0, BC) * RB;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      dma16_buf<0>(rk, dma_k[i], ks + (wid * IPW + i) * 1024);
-      dma16_buf<0>(rv, dma_v[i], vs + (wid * IPW + i) * 1024);
-    }
-  };
   auto issue_one = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
     const int key0 = j * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
+    for (int i = 0; i < IPD; ++i) dma16_buf<0>(r, off[i], st + (dwid * IPD + i) * 1024);
   };
-#if FA_PP2
   // S_j = K_j Q^T into s (false if the wave sees none of the tile's keys), and
   // the online softmax of S_j into P_j (packed bf16).
   f32x16 s[NKB];
@@ -792,91 +786,6 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     }
     l_run += ts;
   };
-#else
-  // S_j -> P_j (packed bf16) with the online softmax; false if the wave sees
-  // none of the tile's keys.
-  auto qk_softmax = [&](int j, const unsigned char* kl) -> bool {
-    const int key0 = j * BC;
-    if (CAUSAL && key0 > q0 + 31) return false;
-    // consecutive MFMAs go to different accumulators (no back-to-back chain)
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32) {
-        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
-        s[kb32] = mfma_bf16(a, qr[kb], s[kb32]);
-      }
-    {
-      constexpr int NM = NKB * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
-#pragma unroll
-      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
-    }
-    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
-      // key = key0 + 4g + rel, rel a compile-time constant per register
-      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
-          if (rel > lim) s[kb32][r] = -INFINITY;
-        }
-    }
-    // P against the running max first; the tile max is only taken when some
-    // lane's partial row sum leaves [0, kSumBound]: a score far above the
-    // running max, or the first tile of the rows (running max still -inf).
-    auto expo = [&](float m) -> float {
-      float t = 0.f;
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t w4[4];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
-            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
-            w4[w] = pack_bf16(e0, e1);
-#if FA_SUM_F32
-            t += e0 + e1;
-#else
-            t = add_bf16_pair(w4[w], t);
-#endif
-          }
-          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
-        }
-      return t;
-    };
-    float ts = expo(m_run);
-    if (__any(!(ts <= kSumBound))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb32 = 0; kb32 < NKB; ++kb32)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      ts = expo(m_run);
-    }
-    l_run += ts;
-    return true;
-  };
-#endif
   auto pv = [&](const unsigned char* vl) {
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32)
@@ -904,13 +813,51 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, PF / 2, 0);
     }
   };
-#if FA_PP2
-  // Phase j: both groups add P_{j-1} V_{j-1} and form S_j = K_j Q^T (32
-  // products); group 0 then runs the softmax of S_j, group 1 ran the softmax
-  // of S_{j-1} first.  So on each SIMD one wave's softmax (VALU) always runs
-  // under the other wave's 32 products.  K_j lives in stage j % 2, V_j in
-  // stage j % 2; phase j loads K_{j+1} and V_j.
+
   bool has_s = false, has_p = false;
+  if constexpr (LATE) {
+  // K_j lives in stage j % 3 of k, V_j in stage j % 3 of v.  Group 0 issues
+  // K_{j+2} and V_{j+1} at the end of phase j; at the start of phase j it
+  // needs K_j and V_{j-1} and may leave K_{j+1} and V_j (issued after them)
+  // in flight.
+  auto step = [&](int j, const unsigned char* kc, const unsigned char* vp, unsigned char* k_load,
+                  unsigned char* v_load) __attribute__((always_inline)) {
+    if (grp == 0) {
+      if (j + 1 < n_tiles) wait_vmem_upto<2 * IPD>();
+      else if (j < n_tiles) wait_vmem_upto<IPD>();
+      else wait_vmem();
+    }
+    barrier_lds();
+    if (grp == 1 && has_s) {
+      softmax(j - 1);
+      has_p = true;
+    }
+    if (has_p) pv(vp);
+    has_p = false;
+    has_s = j < n_tiles && qk(j, kc);
+    if (grp == 0) {
+      if (has_s) {
+        softmax(j);
+        has_p = true;
+        has_s = false;
+      }
+      if (j + 2 < n_tiles) issue_one(kg, dma_k, j + 2, k_load);
+      if (j + 1 < n_tiles) issue_one(vg, dma_v, j + 1, v_load);
+    }
+  };
+  if (grp == 0) {
+    issue_one(kg, dma_k, 0, k0);
+    if (1 < n_tiles) issue_one(kg, dma_k, 1, k1);
+    issue_one(vg, dma_v, 0, v0);
+  }
+  for (int j = 0; j <= n_tiles; j += 3) {
+    step(j, k0, v2, k2, v1);
+    if (j + 1 <= n_tiles) step(j + 1, k1, v0, k0, v2);
+    if (j + 2 <= n_tiles) step(j + 2, k2, v1, k1, v0);
+  }
+  } else {
+  // K_j lives in stage j % 2 of k, V_j in stage j % 2 of v; phase j loads
+  // K_{j+1} and V_j.
   auto step = [&](int j, const unsigned char* kc, const unsigned char* vp, unsigned char* kn,
                   unsigned char* vn) __attribute__((always_inline)) {
     wait_vmem();
@@ -935,36 +882,8 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     step(j, k0, v1, k1, v0);
     if (j + 1 <= n_tiles) step(j + 1, k1, v0, k0, v1);
   }
-#else
-  // K_j lives in stage j % 2, V_j in stage j % 3.
-  auto step = [&](int j, const unsigned char* kc, const unsigned char* vc, const unsigned char* vp,
-                  unsigned char* kn, unsigned char* vn) {
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < n_tiles) issue(j + 1, kn, vn);
-    if (grp == 1 && pend) pv(vp);
-    pend = qk_softmax(j, kc);
-    if (grp == 0 && pend) {
-      pv(vc);
-      pend = false;
-    }
-  };
-
-  issue(0, k0, v0);
-  for (int j = 0; j < n_tiles; j += 6) {
-    step(j, k0, v0, v2, k1, v1);
-    if (j + 1 < n_tiles) step(j + 1, k1, v1, v0, k0, v2);
-    if (j + 2 < n_tiles) step(j + 2, k0, v2, v1, k1, v0);
-    if (j + 3 < n_tiles) step(j + 3, k1, v0, v2, k0, v1);
-    if (j + 4 < n_tiles) step(j + 4, k0, v1, v0, k1, v2);
-    if (j + 5 < n_tiles) step(j + 5, k1, v2, v1, k0, v0);
-  }
-  if (grp == 1 && pend) {
-    const int r = (n_tiles - 1) % 3;
-    pv(r == 0 ? v0 : (r == 1 ? v1 : v2));
   }
 
-#endif
   const float l_tot = sum_halves(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -1485,23 +1404,25 @@ static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int BC>
+template <int D, bool CAUSAL, int BC, bool LATE>
 static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
-  finish_grid(p, PpCfg<D, BC>::BR);
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC>), dim3(p.total), dim3(PpCfg<D, BC>::NT), 0, s, p);
+  using C = PpCfg<D, BC, LATE>;
+  finish_grid(p, C::BR);
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
 // Kernel choice per (head dim, mask), from measurements on MI355X:
-//  * d = 128: ping-pong, 8 waves, 64-key tiles;
-//  * d = 64 non-causal: ping-pong, 128-key tiles;
-//  * d = 64 causal and d = 256: four independent waves per workgroup with
-//    128-row tiles (twice the workgroups of the ping-pong kernel: better
-//    balance for short causal grids; d = 256 does not fit two waves a SIMD).
+//  * d = 128: ping-pong, 8 waves, 64-key tiles, DMA at the start of a phase;
+//  * d = 64 non-causal: ping-pong, 128-key tiles, DMA at the end of a phase;
+//  * d = 64 causal: four independent waves per workgroup with 128-row tiles
+//    (twice the workgroups of the ping-pong kernel: better balance for short
+//    causal grids);
+//  * d = 256: wave pairs splitting the columns of O (two waves a SIMD).
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128>(p, s);
-    case 128: return causal ? launch_pp<128, true, 64>(p, s) : launch_pp<128, false, 64>(p, s);
+    case 64: return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128, true>(p, s);
+    case 128: return causal ? launch_pp<128, true, 64, false>(p, s) : launch_pp<128, false, 64, false>(p, s);
 #if FA_D256_PAIRS
     case 256: return causal ? launch_pairs<256, true>(p, s) : launch_pairs<256, false>(p, s);
 #else
