@@ -166,4 +166,43 @@ __device__ __forceinline__ WorkItem map_work(int block, int total, int n_qt, boo
   return it;
 }
 
+// Persistent grid: `workers` workgroups (one per CU) each loop over several
+// work items, so no workgroup ever waits for the dispatcher (which issues in
+// order and, with causal tiles of uneven length, stalls on a busy XCD while
+// other CUs idle).  The item list (head-major, heaviest causal tile of a head
+// first, as above) is split into 8 contiguous ranges, one per XCD when the
+// counts divide by 8 (workgroup b runs on XCD b % 8); inside its range,
+// worker c takes one item per round in snake order (c, then L-1-c, ...),
+// which balances uneven causal work and keeps an XCD on one or two heads.
+struct PersistentMap {
+  int base, per;   // item range of this worker's group of workers
+  int L, c;        // workers in the group, this worker's index in it
+};
+__device__ __forceinline__ PersistentMap persistent_map(int block, int workers, int total) {
+  PersistentMap m;
+  if (total % 8 == 0 && workers % 8 == 0) {
+    m.per = total >> 3;
+    m.base = (block & 7) * m.per;
+    m.L = workers >> 3;
+    m.c = block >> 3;
+  } else {
+    m.per = total;
+    m.base = 0;
+    m.L = workers;
+    m.c = block;
+  }
+  return m;
+}
+// Item of round r for this worker, or -1 when its share is done.
+__device__ __forceinline__ int persistent_item(const PersistentMap& m, int r) {
+  const int j = r * m.L + ((r & 1) ? m.L - 1 - m.c : m.c);
+  return j < m.per ? m.base + j : -1;
+}
+__device__ __forceinline__ WorkItem item_of(int w, int n_qt) {
+  WorkItem it;
+  it.bh = w / n_qt;
+  it.qt = n_qt - 1 - (w - it.bh * n_qt);
+  return it;
+}
+
 }  // namespace fa

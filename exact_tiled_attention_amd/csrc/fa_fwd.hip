@@ -31,6 +31,7 @@
 // Causal: key tiles past the work-group's last query are never loaded; the
 // mask is applied only on tiles that straddle the diagonal or the sequence
 // end (FA2's causal optimisation, "Flash Attention 2 / 3 とは 2026年版").
+#include <atomic>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -53,6 +54,9 @@
 #endif
 #ifndef FA_SUM_F32
 #define FA_SUM_F32 1
+#endif
+#ifndef FA_PERSIST
+#define FA_PERSIST 1
 #endif
 #ifndef QK_PREFETCH
 #define QK_PREFETCH 8
@@ -629,9 +633,9 @@ struct PpCfg {
   static_assert(2 * IPD < 64, "DMA count must fit the vmcnt field");
 };
 
+// One work item (head, 256-row query tile) of the ping-pong kernel.
 template <int D, bool CAUSAL, int BC_, bool LATE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_pp_kernel(FwdParams p) {
+__device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   using C = PpCfg<D, BC_, LATE>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPD = C::IPD, NKB = C::NKB, NST = C::NST;
   __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILE];
@@ -645,7 +649,6 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wid >> 2;
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
   const int N = p.N;
   const int b = wi.bh / p.H, h = wi.bh - b * p.H;
   const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
@@ -898,6 +901,23 @@ void fwd_bf16_pp_kernel(FwdParams p) {
         *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
       }
     if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// With PERSIST, one workgroup per CU loops over its share of the items (see
+// persistent_map); otherwise one workgroup per item.
+template <int D, bool CAUSAL, int BC_, bool LATE, bool PERSIST>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_pp_kernel(FwdParams p) {
+  if constexpr (PERSIST) {
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total);
+    for (int r = 0;; ++r) {
+      const int w = persistent_item(pm, r);
+      if (w < 0) break;
+      pp_item<D, CAUSAL, BC_, LATE>(p, item_of(w, p.n_qt));
+    }
+  } else {
+    pp_item<D, CAUSAL, BC_, LATE>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
   }
 }
 
@@ -1404,11 +1424,29 @@ static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Compute units of the current device, read once per device.
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int D, bool CAUSAL, int BC, bool LATE>
 static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
   using C = PpCfg<D, BC, LATE>;
   finish_grid(p, C::BR);
-  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE>), dim3(p.total), dim3(C::NT), 0, s, p);
+  const int cus = FA_PERSIST ? cu_count() : 0;
+  if (cus > 0 && p.total > cus) {
+    hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, true>), dim3(cus), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, false>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -142,6 +142,22 @@ def test_forward_running_max_moves(dtype, d, causal):
         assert eo <= tol_o and el <= tol_l, (dtype, d, causal, n, eo, tol_o, el, tol_l)
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 300, 256, 128, True), (1, 300, 256, 128, False),
+                                              (2, 132, 300, 128, True), (1, 260, 512, 64, False)])
+def test_forward_persistent_grid(B, H, N, d, causal):
+    """More work items than compute units: the d=128 and d=64 kernels switch to
+    one workgroup per CU looping over items (item counts that do and do not
+    divide by 8 take the two item maps); every row is compared."""
+    _say(f"persistent grid B={B} H={H} N={N} d={d} causal={causal}")
+    w = syn.Workload("pg", B, H, H, N, d, "bf16", causal, 1.0, 31 + H)
+    x = syn.make_inputs(w)
+    o, lse = _run_fwd(x, causal)
+    o_ref, lse_ref = oracle.forward(x["q_64"], x["k_64"], x["v_64"], x["scale"], causal)
+    eo = _err(o.double().cpu().numpy(), o_ref)
+    el = _err(lse.double().cpu().numpy(), lse_ref)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"], (B, H, N, d, causal, eo, el)
+
+
 def test_forward_is_deterministic():
     w = syn.Workload("det", 1, 4, 4, 1000, 128, "bf16", True, 1.0, 3)
     x = syn.make_inputs(w)
