@@ -22,6 +22,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// The kernels fold the scale into the exponent's FMA and mask with -inf
+// scores, which is only sound for a positive scale (attention's is 1/sqrt(d)).
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+
 bool valid_dtype(int t) { return t == FA_DTYPE_F32 || t == FA_DTYPE_BF16 || t == FA_DTYPE_FP8_E4M3; }
 
 // Shape checks shared by both directions; also guards every size product.
@@ -57,7 +61,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
     case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: non-positive size, H not a multiple of H_kv, or size overflow";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this (dtype, head dim, direction)";
-    case FA_ERR_INVALID_VALUE: return "FA_ERR_INVALID_VALUE: non-finite scale, misaligned pointer, aliasing output, or misplaced descale";
+    case FA_ERR_INVALID_VALUE: return "FA_ERR_INVALID_VALUE: scale not finite and positive, misaligned pointer, aliasing output, or misplaced descale";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error at launch";
   }
@@ -74,7 +78,7 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   if (fp8 && (!q_descale || !k_descale || !v_descale)) return FA_ERR_NULL_POINTER;
   if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
   if (!fa_supported(dtype, d, 0)) return FA_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return FA_ERR_INVALID_VALUE;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
   if (!fp8 && (q_descale || k_descale || v_descale)) return FA_ERR_INVALID_VALUE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return FA_ERR_INVALID_VALUE;
@@ -116,7 +120,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
   if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
   if (!fa_supported(dtype, d, 1)) return FA_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return FA_ERR_INVALID_VALUE;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
   const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
   for (const void* q : ptrs)
     if (!aligned16(q)) return FA_ERR_INVALID_VALUE;

@@ -29,7 +29,8 @@
  *          アテンション" (進化と関連技術).
  * Causal   causal != 0 lets query i see keys 0..i (diagonal included).
  * LSE      LSE[i] = ln sum_{j visible} exp(scale * q_i . k_j)  (natural log).
- * Scale    any finite value; callers normally pass 1/sqrt(d).
+ * Scale    finite and > 0 (FA_ERR_INVALID_VALUE otherwise); callers normally
+ *          pass 1/sqrt(d).
  * Streams  Work is enqueued on `stream` and runs asynchronously; device-side
  *          faults surface at the caller's next synchronisation.
  * Errors   Every entry point validates all arguments on the host before it
@@ -62,8 +63,8 @@ typedef enum {
   FA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                       */
   FA_ERR_INVALID_SHAPE = 2, /* B,H,H_kv,N,d <= 0; H % H_kv != 0; size overflow  */
   FA_ERR_UNSUPPORTED = 3,   /* (dtype, d, direction) has no kernel              */
-  FA_ERR_INVALID_VALUE = 4, /* non-finite scale, misaligned pointer, an output
-                               aliasing an input, descale given for non-fp8    */
+  FA_ERR_INVALID_VALUE = 4, /* scale not finite and > 0, misaligned pointer,
+                               an output aliasing an input, descale for non-fp8 */
   FA_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required          */
   FA_ERR_HIP = 6            /* the HIP runtime reported an error at launch      */
 } fa_status;

@@ -90,6 +90,8 @@ def test_fwd_validation(lib):
     assert fwd(lib, dtype=9) == 3
     assert fwd(lib, scale=float("nan")) == 4
     assert fwd(lib, scale=float("inf")) == 4
+    assert fwd(lib, scale=0.0) == 4                  # a masked -inf score times 0 is NaN
+    assert fwd(lib, scale=-0.125) == 4               # would turn masked scores into +inf
     assert fwd(lib, qs=7 * P) == 4                   # descale on a non-fp8 call
     assert fwd(lib, q=P + 8) == 4                    # misaligned
     assert fwd(lib, lse=P + 4) == 4
@@ -103,6 +105,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, d=256) == 3
     assert bwd(lib, N=0) == 2
     assert bwd(lib, scale=float("nan")) == 4
+    assert bwd(lib, scale=-1.0) == 4
     assert bwd(lib, ws=None) == 5
     assert bwd(lib, ws_bytes=16) == 5
     assert bwd(lib, ws=64 * P + 128) == 5            # not 256-byte aligned
