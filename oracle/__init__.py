@@ -24,6 +24,7 @@ from .attention import (  # noqa: F401
     forward_head,
     forward,
     forward_rows,
+    forward_kvcache,
     backward_head,
     backward,
 )

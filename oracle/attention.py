@@ -103,6 +103,44 @@ def forward(q, k, v, scale=None, causal=True):
     return o, lse
 
 
+def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
+    """Attention of a few new queries against a KV cache.
+
+    q [B,H,N_q,d]; k/v [B,H_kv,N_kv,d] hold the cache, of which batch b uses
+    the first kv_len[b] rows (all N_kv when kv_len is None).  The decode case
+    of "FlashAttentionとは？…" (短い系列の効果とデコード向け最適化の違い): the
+    query side is short (one token per step) and the whole cache is read.
+    The N_q queries are taken to be the last N_q positions of the sequence,
+    so query i sits at position kv_len - N_q + i and, under the causal mask
+    of scores_rows, sees keys 0..kv_len - N_q + i.  A row that sees no key
+    (an empty cache, or kv_len < N_q under the mask) has no softmax; its
+    output is taken as zero and its LSE as -inf (the log of an empty sum).
+    Returns O [B,H,N_q,d_v] and LSE [B,H,N_q].
+    """
+    B, H, n_q, d = q.shape
+    H_kv, n_kv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lens = [n_kv] * B if kv_len is None else [int(x) for x in kv_len]
+    if len(lens) != B or any(not 0 <= n <= n_kv for n in lens):
+        raise ValueError("kv_len must hold B values in [0, N_kv]")
+    o = np.zeros((B, H, n_q, v.shape[3]), dtype=np.float64)
+    lse = np.full((B, H, n_q), -np.inf)
+    for b in range(B):
+        n = lens[b]
+        pos = n - n_q + np.arange(n_q)                    # positions of the queries
+        n_seen = np.clip(pos + 1, 0, n) if causal else np.full(n_q, n)
+        rows = np.flatnonzero(n_seen > 0)
+        if rows.size == 0:
+            continue
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            s = scores_rows(q[b, h, rows], k[b, kv, :n], scale, causal, pos[rows])
+            p, lse[b, h, rows] = softmax_rows(s)
+            o[b, h, rows] = p @ v[b, kv, :n]
+    return o, lse
+
+
 def backward_head(q, k, v, do, scale, causal):
     """Gradients of L = sum(O * dO) with respect to Q, K, V for one head.
 

@@ -2,7 +2,8 @@
 
 Each ``pin_*`` takes an implementation namespace ``impl`` exposing
 ``forward(q,k,v,scale,causal)``, ``forward_rows(q,k,v,scale,causal,rows)``,
-``softmax_rows(s)``, ``scores_rows(...)`` and ``backward(q,k,v,do,scale,causal)``
+``softmax_rows(s)``, ``scores_rows(...)``, ``backward(q,k,v,do,scale,causal)`` and
+``forward_kvcache(q,k,v,kv_len,scale,causal)``
 (the oracle, or a deliberately broken copy of it in the mutation test) and
 raises AssertionError when the implementation disagrees with:
 
@@ -11,7 +12,10 @@ raises AssertionError when the implementation disagrees with:
 * invariants (row sums of P, permutation of K/V rows, shifts of K and V);
 * an independent scalar brute force written here with ``math.exp``/``math.fsum``;
 * central finite differences of L = sum(O * dO) for the gradients;
-* gradient identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+* gradient identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i);
+* for the KV-cache forward: a scalar brute force over ragged cache lengths,
+  the square case (ordinary attention), cache rows past the length being
+  ignored, identical keys, and the newest query seeing the whole cache.
 """
 from __future__ import annotations
 
@@ -175,6 +179,109 @@ def pin_forward_rows(impl):
         assert np.max(np.abs(lrow - lf[0, 0, rows])) < 1e-14
 
 
+# ---------------------------------------------------------- KV-cache decode ---
+
+def brute_force_kvcache(q, k, v, kv_len, scale, causal):
+    """Scalar loops: query i of batch b stands at position kv_len[b] - N_q + i."""
+    B, H, n_q, d = q.shape
+    H_kv = k.shape[1]
+    g = H // H_kv
+    o = np.zeros((B, H, n_q, v.shape[3]))
+    lse = np.full((B, H, n_q), -math.inf)
+    for b, h, i in itertools.product(range(B), range(H), range(n_q)):
+        n = int(kv_len[b])
+        last = min(n - 1, n - n_q + i) if causal else n - 1
+        js = list(range(last + 1))
+        if not js:
+            continue
+        kv = h // g
+        s = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, kv, j, t]) for t in range(d)) for j in js]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = math.fsum(w)
+        lse[b, h, i] = mx + math.log(tot)
+        for t in range(v.shape[3]):
+            o[b, h, i, t] = math.fsum(wj * float(v[b, kv, j, t]) for wj, j in zip(w, js)) / tot
+    return o, lse
+
+
+def pin_kvcache_brute_force(impl):
+    """Ragged cache lengths (including 0 and lengths below N_q), GQA, both masks."""
+    rng = _rng(21)
+    cases = [(1, 1, 1, 1, 9, 4, [9]), (2, 4, 2, 3, 11, 5, [11, 2]), (3, 6, 3, 2, 7, 3, [0, 1, 7]),
+             (1, 2, 1, 5, 16, 8, [13])]
+    for (B, H, H_kv, n_q, n_kv, d, lens), causal in itertools.product(cases, (False, True)):
+        q = rng.standard_normal((B, H, n_q, d)) * 1.5
+        k = rng.standard_normal((B, H_kv, n_kv, d)) * 1.5
+        v = rng.standard_normal((B, H_kv, n_kv, d))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = impl.forward_kvcache(q, k, v, lens, scale, causal)
+        o_b, lse_b = brute_force_kvcache(q, k, v, lens, scale, causal)
+        assert np.max(np.abs(o - o_b)) < 1e-13, (B, H, n_q, lens, causal)
+        fin = np.isfinite(lse_b)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.max(np.abs(lse[fin] - lse_b[fin]), initial=0.0) < 1e-13
+
+
+def pin_kvcache_square_case(impl):
+    """N_q = N_kv with the full cache is ordinary attention (top-left = bottom-right)."""
+    rng = _rng(22)
+    q = rng.standard_normal((2, 4, 9, 5))
+    k, v = rng.standard_normal((2, 2, 9, 5)), rng.standard_normal((2, 2, 9, 5))
+    for causal in (False, True):
+        o1, l1 = impl.forward_kvcache(q, k, v, None, 0.6, causal)
+        o2, l2 = impl.forward(q, k, v, 0.6, causal)
+        assert np.max(np.abs(o1 - o2)) < 1e-14 and np.max(np.abs(l1 - l2)) < 1e-14
+
+
+def pin_kvcache_tail_ignored(impl):
+    """Cache rows at or past kv_len never matter; kv_len = n equals a cache of n rows."""
+    rng = _rng(23)
+    q = rng.standard_normal((2, 2, 3, 4))
+    k, v = rng.standard_normal((2, 1, 12, 4)), rng.standard_normal((2, 1, 12, 4))
+    lens = [7, 12]
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 7:] = 1e3
+    v2[0, :, 7:] = -1e3
+    for causal in (False, True):
+        o1, l1 = impl.forward_kvcache(q, k, v, lens, 0.5, causal)
+        o2, l2 = impl.forward_kvcache(q, k2, v2, lens, 0.5, causal)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        o3, l3 = impl.forward_kvcache(q[:1], k[:1, :, :7], v[:1, :, :7], None, 0.5, causal)
+        assert np.max(np.abs(o3 - o1[:1])) < 1e-15 and np.max(np.abs(l3 - l1[:1])) < 1e-15
+
+
+def pin_kvcache_identical_keys(impl):
+    """Identical keys: row i averages the V rows it sees, LSE = q.k*scale + ln(count)."""
+    rng = _rng(24)
+    n_q, n_kv, d = 4, 10, 3
+    q = rng.standard_normal((1, 1, n_q, d))
+    k = np.repeat(rng.standard_normal((1, 1, 1, d)), n_kv, axis=2)
+    v = rng.standard_normal((1, 1, n_kv, d))
+    for n, causal in itertools.product((10, 6, 2), (False, True)):
+        o, lse = impl.forward_kvcache(q, k, v, [n], 0.8, causal)
+        for i in range(n_q):
+            seen = min(n, n - n_q + i + 1) if causal else n
+            if seen <= 0:
+                assert np.all(o[0, 0, i] == 0) and lse[0, 0, i] == -math.inf
+                continue
+            assert np.max(np.abs(o[0, 0, i] - v[0, 0, :seen].mean(axis=0))) < 1e-13
+            want = 0.8 * float(q[0, 0, i] @ k[0, 0, 0]) + math.log(seen)
+            assert abs(lse[0, 0, i] - want) < 1e-12
+
+
+def pin_kvcache_last_query_sees_all(impl):
+    """The newest query sees the whole cache, so the mask cannot change its row."""
+    rng = _rng(25)
+    q = rng.standard_normal((2, 4, 3, 6))
+    k, v = rng.standard_normal((2, 2, 8, 6)), rng.standard_normal((2, 2, 8, 6))
+    oc, lc = impl.forward_kvcache(q, k, v, [8, 5], 0.4, True)
+    on, ln = impl.forward_kvcache(q, k, v, [8, 5], 0.4, False)
+    assert np.max(np.abs(oc[:, :, -1] - on[:, :, -1])) < 1e-15
+    assert np.max(np.abs(lc[:, :, -1] - ln[:, :, -1])) < 1e-15
+    assert np.max(np.abs(oc[:, :, 0] - on[:, :, 0])) > 1e-3   # earlier rows do differ
+
+
 # --------------------------------------------------------------- backward ---
 
 def _loss(impl, q, k, v, do, scale, causal):
@@ -231,5 +338,7 @@ def pin_gradient_identities(impl):
 FORWARD_PINS = [pin_rows_sum_to_one, pin_identical_keys, pin_dominant_key, pin_causal_row0,
                 pin_permutation_invariance, pin_shifts, pin_brute_force, pin_worked_example,
                 pin_forward_rows]
+KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
+                pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]
 BACKWARD_PINS = [pin_finite_differences, pin_gradient_identities]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + KVCACHE_PINS + BACKWARD_PINS

@@ -55,6 +55,33 @@ def test_matches_torch_sdpa_fp64(shape, causal):
     assert np.max(np.abs(dv - v.grad.numpy())) < 1e-11
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 1, 97, 32), (3, 4, 4, 5, 40, 16), (1, 6, 2, 7, 7, 8)])
+def test_kvcache_matches_torch_sdpa_fp64(shape, causal):
+    """Library cross-check of the KV-cache forward: torch's CPU SDPA in float64 with a
+    boolean mask built here (query i of N_q sees keys j <= len - N_q + i)."""
+    B, H, H_kv, n_q, n_kv, d = shape
+    g = torch.Generator().manual_seed(sum(shape) + 7 * causal)
+    q = torch.randn(B, H, n_q, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, H_kv, n_kv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H_kv, n_kv, d, generator=g, dtype=torch.float64)
+    lens = torch.randint(n_q, n_kv + 1, (B,), generator=g).tolist()
+    lens[0] = n_kv
+    o, lse = oracle.forward_kvcache(q.numpy(), k.numpy(), v.numpy(), lens, None, causal)
+    rep = H // H_kv
+    for b, n in enumerate(lens):
+        kk = k[b:b + 1, :, :n].repeat_interleave(rep, 1)
+        vv = v[b:b + 1, :, :n].repeat_interleave(rep, 1)
+        mask = torch.ones(n_q, n, dtype=torch.bool)
+        if causal:
+            mask = mask.tril(diagonal=n - n_q)
+        ref = F.scaled_dot_product_attention(q[b:b + 1], kk, vv, attn_mask=mask)
+        assert np.max(np.abs(o[b] - ref[0].numpy())) < 1e-12
+        s = (q[b:b + 1] @ kk.transpose(-1, -2)) / math.sqrt(d)
+        s = s.masked_fill(~mask, float("-inf"))
+        assert np.max(np.abs(lse[b] - torch.logsumexp(s, -1)[0].numpy())) < 1e-12
+
+
 def _page_fp32_errors():
     path = os.path.join(os.path.dirname(__file__), "golden", "cpu_sdpa_fp32_error.txt")
     out = {}
@@ -101,6 +128,11 @@ MUTANTS = {
     "dk_missing_scale": ("dk += scale * (ds.T @ q[rid])", "dk += (ds.T @ q[rid])"),
     "dv_uses_ds": ("dv += p.T @ do[rid]", "dv += ds.T @ do[rid]"),
     "gqa_grads_overwrite": ("dk[b, kv] += gk", "dk[b, kv] = gk"),
+    "kvcache_top_left": ("pos = n - n_q + np.arange(n_q)", "pos = np.arange(n_q)"),
+    "kvcache_off_by_one": ("pos = n - n_q + np.arange(n_q)", "pos = n - n_q + 1 + np.arange(n_q)"),
+    "kvcache_whole_cache": ("s = scores_rows(q[b, h, rows], k[b, kv, :n],", "s = scores_rows(q[b, h, rows], k[b, kv],"),
+    "kvcache_empty_rows_nan": ("rows = np.flatnonzero(n_seen > 0)", "rows = np.arange(n_q)"),
+    "kvcache_v_whole_cache": ("o[b, h, rows] = p @ v[b, kv, :n]", "o[b, h, rows] = p @ v[b, kv, :p.shape[1]][::-1]"),
 }
 
 
