@@ -14,8 +14,10 @@ The JSON line also carries:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload on this host's cores;
   extra         the other kernels measured the same way: the headline-size
-                causal bf16 d=128 forward, the fp32 and fp8 forwards, and the
-                bf16 backward (fwd+bwd) at its full size.
+                causal bf16 d=128 forward, the fp32 and fp8 forwards, the
+                bf16 backward (fwd+bwd) at its full size, and the KV-cache
+                (decode) forward as the rate it reads the cache at, against
+                the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -34,9 +36,10 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # dense MFMA, 256 
 HBM_GBS = 8000.0
 STEP = ["C2a", "C2a_nc", "C2b"]
 EXTRA_FWD = ["Ta", "Ta_gqa", "Tb", "Tc", "C1", "C3", "C5"]
+EXTRA_KV = ["D1", "D1_ragged"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp")]
+                  for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_kvcache.hip", "fa_common.hpp")]
 
 
 def source_hash() -> str:
@@ -97,6 +100,37 @@ class Case:
         import exact_tiled_attention_amd as fa
         fa.fa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.w.causal,
                   scale=self.scale, workspace=self.ws, dq=self.dq, dk=self.dk, dv=self.dv)
+
+
+class KvCase:
+    """Device-resident query, caches and workspace of one decode workload."""
+
+    def __init__(self, name, dev):
+        import torch
+        import synthetic as syn
+        import exact_tiled_attention_amd as fa
+        self.w = w = syn.KV_WORKLOADS[name]
+        x = syn.make_kvcache_inputs(w)
+        self.lens = x["lens"]
+        self.scale = x["scale"]
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.kv_len = x["kv_len"].to(dev) if x["kv_len"] is not None else None
+        self.o = torch.empty(w.B, w.H, w.N_q, w.d, device=dev, dtype=torch.bfloat16)
+        self.lse = torch.empty(w.B, w.H, w.N_q, device=dev, dtype=torch.float32)
+        need = fa.fa_fwd_kvcache_workspace_bytes(w.B, w.H, w.H_kv, w.N_q, w.N_kv, w.d, 1)
+        self.ws = torch.empty(need, device=dev, dtype=torch.uint8)
+
+    def fwd(self):
+        import exact_tiled_attention_amd as fa
+        fa.fa_fwd_kvcache(self.q, self.k, self.v, self.kv_len, causal=self.w.causal, scale=self.scale,
+                          out=self.o, lse=self.lse, workspace=self.ws)
+
+    def report(self, ms):
+        gbs = self.w.cache_bytes(self.lens) / (ms * 1e-3) / 1e9
+        return {"kernel": f"kvcache_bf16_d{self.w.d}", "ms": round(ms, 4),
+                "cache_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_GBS, 4),
+                "cache_bytes": self.w.cache_bytes(self.lens),
+                "tflops": round(self.w.flops(self.lens) / (ms * 1e-3) / 1e12, 3)}
 
 
 def log(msg):
@@ -207,6 +241,20 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
         return
 
+    import synthetic as syn
+    if args.only in syn.KV_WORKLOADS:
+        # decode alone (profiling runs): split + combine kernels per call
+        c = KvCase(args.only, dev)
+        xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
+        rep = c.report(median(xs))
+        log(f"{args.only}: {rep}")
+        print(json.dumps({"metric": "KV-cache read rate (GB/s) of the decode forward",
+                          "value": rep["cache_GBps"], "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": rep["ms"],
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": args.only}, "decode": rep}))
+        return
+
     names = [args.only] if args.only else STEP
     cases = [Case(n, dev, backward=syn_workload(n).backward and bool(args.only)) for n in names]
     step_flops = sum(c.w.flops_fwd() + (c.w.flops_bwd() if c.backward else 0.0) for c in cases)
@@ -277,6 +325,12 @@ def main():
             tf = c.w.flops_fwd() / (ms * 1e-3) / 1e12
             extra[name] = {"kernel": kernel_name(c.w), "ms": round(ms, 4), "tflops": round(tf, 2),
                            "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
+            del c
+            torch.cuda.empty_cache()
+        for name in EXTRA_KV:
+            log(f"extra: {name}")
+            c = KvCase(name, dev)
+            extra[name] = c.report(median(time_launches(c.fwd, reps=20, warmup=3)))
             del c
             torch.cuda.empty_cache()
         log("extra: C4 forward + backward")

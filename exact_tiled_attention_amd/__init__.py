@@ -15,8 +15,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_supported", "fa_status_string",
-           "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+           "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
+           "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -24,7 +25,9 @@ FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE",
                 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_INVALID_VALUE", 5: "FA_ERR_WORKSPACE",
                 6: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_supported", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+            "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
+            "fa_status_string")
 
 _lib = None
 
@@ -56,6 +59,12 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_supported.argtypes = [i, i, i]
     lib.fa_supported.restype = i
+    lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_kvcache.restype = i
+    lib.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_kvcache_workspace_bytes.restype = sz
+    lib.fa_kvcache_supported.argtypes = [i, i]
+    lib.fa_kvcache_supported.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -69,6 +78,14 @@ def fa_status_string(code: int) -> str:
 
 def fa_supported(dtype: int, d: int, backward: bool) -> bool:
     return bool(load_library().fa_supported(int(dtype), int(d), int(bool(backward))))
+
+
+def fa_kvcache_supported(dtype: int, d: int) -> bool:
+    return bool(load_library().fa_kvcache_supported(int(dtype), int(d)))
+
+
+def fa_fwd_kvcache_workspace_bytes(B, H, H_kv, N_q, N_kv, d, dtype=FA_DTYPE_BF16) -> int:
+    return int(load_library().fa_fwd_kvcache_workspace_bytes(B, H, H_kv, N_q, N_kv, d, int(dtype)))
 
 
 def fa_bwd_workspace_bytes(B, H, H_kv, N, d, dtype=FA_DTYPE_BF16) -> int:
@@ -165,3 +182,48 @@ def fa_bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None,
                       B, H, H_kv, N, d, float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, kv_len=None, causal: bool = True, scale: float | None = None,
+                   out=None, lse=None, want_lse: bool = True, workspace=None):
+    """O, LSE of N_q new queries against a KV cache (decode).
+
+    q [B, H, N_q, d]; k_cache, v_cache [B, H_kv, N_kv, d] (capacity N_kv);
+    kv_len: int32 device tensor [B] of cache rows in use, or None for N_kv.
+    Returns (o, lse); lse is None if not wanted.
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, H, N_q, d], the caches [B, H_kv, N_kv, d]")
+    B, H, N_q, d = q.shape
+    _, H_kv, N_kv, dk = k_cache.shape
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k_cache.shape)} "
+                         f"v {tuple(v_cache.shape)}")
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and the caches must be contiguous device tensors")
+    if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
+        raise ValueError("q and the caches must share one dtype")
+    if kv_len is not None and (kv_len.dtype != torch.int32 or not kv_len.is_cuda
+                               or not kv_len.is_contiguous() or tuple(kv_len.shape) != (B,)):
+        raise ValueError("kv_len must be a contiguous int32 device tensor of shape [B]")
+    codes = DTYPE_CODES()
+    if q.dtype not in codes:
+        raise FaError(3, f"unsupported dtype {q.dtype}")
+    dt = codes[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, H, N_q, d, device=q.device, dtype=torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, N_q, device=q.device, dtype=torch.float32)
+    need = int(lib.fa_fwd_kvcache_workspace_bytes(B, H, H_kv, N_q, N_kv, d, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    code = lib.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(out),
+                              _ptr(lse), _ptr(workspace), workspace.numel(), B, H, H_kv, N_q, N_kv,
+                              d, float(scale), int(bool(causal)), dt, _stream())
+    _check(code)
+    return out, lse

@@ -153,4 +153,60 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_kvcache_supported(fa_dtype dtype, int d) {
+  return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128 || d == 256);
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d,
+                                      fa_dtype dtype) {
+  if (!valid_dtype(dtype) || !fa_kvcache_supported(dtype, d)) return 0;
+  if (check_shape(B, H, H_kv, N_q, d) != FA_OK || check_shape(B, H_kv, H_kv, N_kv, d) != FA_OK) return 0;
+  return fa::kv_plan(B, H, H_kv, N_q, N_kv, d).ws_bytes;
+}
+
+fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache, const int* kv_len,
+                         void* O, float* LSE, void* workspace, size_t workspace_bytes, int B, int H,
+                         int H_kv, int N_q, int N_kv, int d, float scale, int causal, fa_dtype dtype,
+                         hipStream_t stream) {
+  if (!Q || !K_cache || !V_cache || !O) return FA_ERR_NULL_POINTER;
+  if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
+  if (fa_status s = check_shape(B, H, H_kv, N_q, d); s != FA_OK) return s;
+  if (fa_status s = check_shape(B, H_kv, H_kv, N_kv, d); s != FA_OK) return s;
+  // one combine workgroup per query row
+  if ((unsigned long long)B * H * N_q > 0x7fffffffull) return FA_ERR_INVALID_SHAPE;
+  if (!fa_kvcache_supported(dtype, d)) return FA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
+  if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) || !aligned16(LSE) ||
+      (reinterpret_cast<uintptr_t>(kv_len) & 3u))
+    return FA_ERR_INVALID_VALUE;
+  const fa::KvPlan plan = fa::kv_plan(B, H, H_kv, N_q, N_kv, d);
+  if (!workspace || workspace_bytes < plan.ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return FA_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(dtype);
+  const size_t nq = (size_t)B * H * N_q * d * eb, nkv = (size_t)B * H_kv * N_kv * d * eb;
+  const size_t ob = (size_t)B * H * N_q * d * out_bytes(dtype), lb = LSE ? (size_t)B * H * N_q * 4 : 0;
+  const size_t klb = kv_len ? (size_t)B * 4 : 0;
+  const void* ins[] = {Q, K_cache, V_cache, kv_len};
+  const size_t insz[] = {nq, nkv, nkv, klb};
+  void* outs[] = {O, LSE, workspace};
+  const size_t outsz[] = {ob, lb, plan.ws_bytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_VALUE;
+  }
+
+  fa::KvParams p{};
+  p.q = Q; p.k = K_cache; p.v = V_cache; p.kv_len = kv_len; p.o = O; p.lse = LSE;
+  p.part_lse = (float*)workspace;
+  p.part_o = (float*)((char*)workspace + plan.lse_bytes);
+  p.B = B; p.H = H; p.H_kv = H_kv; p.Nq = N_q; p.Nkv = N_kv;
+  p.G = plan.G; p.R = plan.R; p.n_rg = plan.n_rg;
+  p.S = plan.S; p.chunk = plan.chunk; p.nw = plan.nw;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_kvcache_bf16(d, causal != 0, p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -376,31 +376,6 @@ struct Bf16Cfg {
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
   static_assert(2 * IPW * (NST - 2) < 64, "DMA count must fit the vmcnt field");
 };
-// Wait until at most N of this wave's vector-memory operations are in flight
-// (they complete in issue order), N a compile-time constant < 64.
-template <int N>
-__device__ __forceinline__ void wait_vmem_upto() {
-  // s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | (((N >> 4) & 3) << 14));
-}
-// XOR swizzles of the 16-byte units of a K or V row in LDS (the DMA writes
-// rows unpadded).  They were chosen by measuring the operand reads on MI355X
-// (rocprof-free microbenchmarks of the exact access patterns):
-//  * K operand reads (16 bytes per lane, lanes 0-15 on rows r..r+15 of one
-//    logical unit): row bit 0 -> unit bit 3, row bits 1-3 -> unit bits 0-2
-//    reaches the full LDS rate; XOR with (r & 15) loses ~25%.  Rows of 128
-//    bytes already alternate bank halves, so there u ^ ((r >> 1) & 7).
-//  * transposing V reads (4 rows x 32 bytes per 16 lanes): row bit 0 -> unit
-//    bit 3, row bit 1 -> unit bit 2 (128-byte rows: row bit 1 -> unit bit 2).
-template <int RB>
-__device__ __forceinline__ int k_swz(int row, int u) {
-  return RB == 128 ? (u ^ ((row >> 1) & 7)) : (u ^ ((row >> 1) & 7) ^ ((row & 1) << 3));
-}
-template <int RB>
-__device__ __forceinline__ int v_swz(int row, int u) {
-  return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ (((row & 1) << 3) | ((row & 2) << 1)));
-}
-
 template <int D, bool CAUSAL, int NW, int BC_, int NST>
 __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const WorkItem wi) {
   using C = Bf16Cfg<D, NW, BC_, NST>;

@@ -42,11 +42,36 @@ struct BwdParams {
   float scale_log2;    // scale * log2(e)
 };
 
+// Attention of N_q new queries against a KV cache, split over the cache.
+struct KvParams {
+  const void* q;       // [B][H][Nq][d]
+  const void* k;       // [B][H_kv][Nkv][d]
+  const void* v;
+  const int* kv_len;   // [B] rows of the cache in use, or null (all Nkv)
+  void* o;             // [B][H][Nq][d]
+  float* lse;          // [B][H][Nq] or null
+  float* part_lse;     // workspace: [B*H_kv][S][R] chunk logsumexp (base 2, scaled)
+  float* part_o;       // workspace: [B*H_kv][S][R][d] chunk outputs (normalised)
+  int B, H, H_kv, Nq, Nkv;
+  int G, R, n_rg;      // heads per group, rows per group (G*Nq), 32-row groups
+  int S, chunk, nw;    // chunks per group, keys per chunk, waves per workgroup
+  float scale_log2;
+};
+
+// Chunking of a KV-cache problem: a pure function of the shape.
+struct KvPlan {
+  int G, R, n_rg, S, chunk, nw;
+  size_t lse_bytes;    // offset of part_o in the workspace (256-aligned)
+  size_t ws_bytes;     // total workspace
+};
+KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d);
+
 // Each returns hipSuccess or the launch error; unsupported shapes never reach
 // them (the C ABI validates first).
 hipError_t launch_fwd_f32(int d, bool causal, FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_fp8(int d, bool causal, FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(int d, bool causal, BwdParams& p, hipStream_t s);
+hipError_t launch_kvcache_bf16(int d, bool causal, KvParams& p, hipStream_t s);
 
 }  // namespace fa

@@ -1,0 +1,399 @@
+// Attention of a few new queries against a long KV cache (decode), gfx950.
+//
+// With one (or a few) queries per head the score matrix is a handful of rows
+// and the kernel's cost is reading the cache: every K and V row is read once
+// and used by the G * N_q query rows of its GQA group, a few flops per byte,
+// far below the MFMA/HBM ridge.  So the work is split over the cache
+// instead of over queries -- the split of the KV-cache read across thread
+// blocks that "FlashAttentionとは？…" describes for decode (短い系列の効果と
+// デコード向け最適化の違い) -- into enough independent pieces to keep every CU's
+// memory pipe full, and a second kernel merges the pieces.
+//
+// Split kernel.  One wave owns all query rows of one GQA group (32 rows per
+// row group: row r = g * N_q + i is query i of the group's head g) and one
+// contiguous chunk of the cache.  It streams its chunk through its own LDS
+// stages by DMA, 32 keys per tile, NST tiles deep, with no workgroup barrier:
+// each wave waits only for its own loads, so a slow wave never holds up
+// another.  Per tile it forms S^T = K Q^T with one MFMA chain (one query row
+// per lane, as in the prefill kernels), masks, applies the online softmax and
+// adds P V into an fp32 accumulator.  It writes its chunk's normalised output
+// and base-2 logsumexp to the workspace.
+//
+// Combine kernel.  Per query row, the chunk results (O_s, lse_s) merge as
+//   lse = log2 sum_s 2^lse_s,   O = sum_s 2^(lse_s - lse) O_s,
+// the same rescaling the online softmax applies between tiles ("Flash
+// Attentionとは？…", 最大値と正規化項を持ち回るオンラインsoftmaxの再スケール),
+// here between chunks.
+//
+// Masking: batch b uses the first kv_len[b] cache rows (clamped to
+// [0, N_kv]); the N_q queries are the last N_q positions, so under the causal
+// mask query i sees keys 0 .. kv_len - N_q + i.  A row that sees no key gets
+// O = 0 and LSE = -inf.
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+#ifndef FA_KV_NW64
+#define FA_KV_NW64 4
+#endif
+#ifndef FA_KV_NST64
+#define FA_KV_NST64 4
+#endif
+#ifndef FA_KV_NW128
+#define FA_KV_NW128 4
+#endif
+#ifndef FA_KV_NST128
+#define FA_KV_NST128 2
+#endif
+#ifndef FA_KV_NW256
+#define FA_KV_NW256 2
+#endif
+#ifndef FA_KV_NST256
+#define FA_KV_NST256 2
+#endif
+
+// Chunks per resident wave slot, and the smallest chunk (in 32-key tiles).
+#ifndef FA_KV_OVERSUB
+#define FA_KV_OVERSUB 1
+#endif
+#ifndef FA_KV_MIN_TILES
+#define FA_KV_MIN_TILES 4
+#endif
+
+template <int D>
+struct KvCfg;
+// Waves per workgroup and LDS stages per wave, sized so one workgroup's
+// stages fill about 128 KB of the CU's 160 KB of LDS.
+template <> struct KvCfg<64> { static constexpr int NW = FA_KV_NW64, NST = FA_KV_NST64; };
+template <> struct KvCfg<128> { static constexpr int NW = FA_KV_NW128, NST = FA_KV_NST128; };
+template <> struct KvCfg<256> { static constexpr int NW = FA_KV_NW256, NST = FA_KV_NST256; };
+
+template <int D>
+struct KvTile {
+  static constexpr int NW = KvCfg<D>::NW, NST = KvCfg<D>::NST;
+  static constexpr int BC = 32;              // keys per tile
+  static constexpr int RB = D * 2;           // bytes per K/V row
+  static constexpr int TILE = BC * RB;       // bytes of one K (or V) tile
+  static constexpr int IPT = TILE / 1024;    // 1 KB DMA issues per tile and tensor
+  static constexpr int STAGE = 2 * TILE;     // K tile, then V tile
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  // vmcnt field: all later tiles plus this tile's V may be outstanding
+  static_assert((NST - 1) * 2 * IPT + IPT < 64, "DMA count must fit the vmcnt field");
+};
+
+__device__ __forceinline__ int cache_len(const KvParams& p, int b) {
+  return p.kv_len ? min(max(p.kv_len[b], 0), p.Nkv) : p.Nkv;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(KvCfg<D>::NW * 64) void kv_split_kernel(KvParams p) {
+  using T = KvTile<D>;
+  constexpr int NW = T::NW, NST = T::NST, BC = T::BC, RB = T::RB, IPT = T::IPT;
+  // One array per stage: the compiler then sees that a DMA into one stage
+  // never aliases the reads of another and waits only for what it must.
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[NW * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[NW * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[NST > 2 ? NW * T::STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[NST > 3 ? NW * T::STAGE : 1];
+
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 31, g = lane >> 5;
+  // block -> (b * H_kv + kv head, workgroup split, row group)
+  const int wg_per = p.S / NW;
+  const int rg = blockIdx.x % p.n_rg;
+  const int rest = blockIdx.x / p.n_rg;
+  const int wgs = rest % wg_per;
+  const int bkv = rest / wg_per;
+  const int b = bkv / p.H_kv, kvh = bkv - b * p.H_kv;
+  const int s = wgs * NW + wid;              // this wave's chunk
+  const int L = cache_len(p, b);
+  const int k_begin = s * p.chunk;
+  if (k_begin >= L) return;                  // empty chunk: the combine skips it
+  const int k_end = min(L, k_begin + p.chunk);
+  const int n_t = (k_end - k_begin + BC - 1) / BC;
+
+  // This lane's query row; lanes past the group's rows compute on zeros.
+  const int r = rg * 32 + lr;
+  const bool row_ok = r < p.R;
+  const int gi = row_ok ? r / p.Nq : 0;
+  const int qi = row_ok ? r - gi * p.Nq : p.Nq - 1;
+  const int h = kvh * p.G + gi;
+  // last visible key of the row, and the smallest one over the group
+  const int lim = CAUSAL ? min(L - p.Nq + qi, L - 1) : L - 1;
+  const int lim_lo = CAUSAL ? L - p.Nq : L - 1;
+
+  bf16x8 qr[D / 16];
+  {
+    const unsigned char* qrow = (const unsigned char*)p.q + (((size_t)b * p.H + h) * p.Nq + qi) * RB;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      bf16x8 x = {};
+      if (row_ok) x = *(const bf16x8*)(qrow + (kb * 16 + 8 * g) * 2);
+      qr[kb] = x;
+    }
+  }
+
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * p.Nkv * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * p.Nkv * RB;
+  int dma_k[IPT], dma_v[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int byte = i * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;   // the swizzles are involutions
+    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
+  }
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8, NVO = D / 32 < 4 ? D / 32 : 4;
+  int koff[NKO];
+#pragma unroll
+  for (int kb = 0; kb < NKO; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  const int s16 = lane & 15, G4 = lane >> 4;
+  const int vrow = 4 * (G4 >> 1) + (s16 >> 2);
+  int voff[NVO];
+#pragma unroll
+  for (int db = 0; db < NVO; ++db)
+    voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G4 & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  auto stage = [&](int u) -> unsigned char* {
+    unsigned char* base = u == 0 ? st0 : (u == 1 ? st1 : (u == 2 ? st2 : st3));
+    return base + wid * T::STAGE;
+  };
+  auto issue = [&](int t, unsigned char* st) {
+    const int key0 = k_begin + t * BC;
+    const int bytes = min(L - key0, BC) * RB;   // rows past the cache length read as zero
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) dma16_buf_nt(rk, dma_k[i], st + i * 1024);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) dma16_buf_nt(rv, dma_v[i], st + T::TILE + i * 1024);
+  };
+
+  const float c = p.scale_log2;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // LATER = tiles issued after this one; their DMAs may stay in flight.
+  auto consume = [&](int t, const unsigned char* kl, auto later_c) __attribute__((always_inline)) {
+    constexpr int LATER = decltype(later_c)::value;
+    const unsigned char* vl = kl + T::TILE;
+    const int key0 = k_begin + t * BC;
+    wait_vmem_upto<LATER * 2 * IPT + IPT>();          // this tile's K has landed
+    f32x16 sc = {};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      const bf16x8 a = *(const bf16x8*)(kl + (kb / NKO) * 256 + koff[kb % NKO]);
+      sc = mfma_bf16(a, qr[kb], sc);
+    }
+    if (key0 + BC - 1 > lim_lo) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int key = key0 + 8 * (q >> 2) + 4 * g + (q & 3);
+        if (key > lim) sc[q] = -INFINITY;
+      }
+    }
+    // P against the running max; the max is taken (and the output rescaled)
+    // only when some lane's partial sum leaves [0, kSumBound], which also
+    // catches rows that have not seen a key yet (running max -inf).
+    bf16x8 pk[2];
+    auto expo = [&](float m) __attribute__((always_inline)) -> float {
+      float tsum = 0.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(fmaf(sc[half * 8 + 2 * w], c, -m));
+          const float e1 = fast_exp2(fmaf(sc[half * 8 + 2 * w + 1], c, -m));
+          w4[w] = pack_bf16(e0, e1);
+          tsum += e0 + e1;
+        }
+        pk[half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+      }
+      return tsum;
+    };
+    float ts = expo(m_run);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sc[q]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      // A row with no visible key so far keeps m = -inf, l = 0, O = 0; its
+      // exponentials are then taken against 0 so that masked scores give 0.
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[i][q] *= alpha;
+      ts = expo(none ? 0.f : m_new);
+    }
+    l_run += ts;
+    wait_vmem_upto<LATER * 2 * IPT>();                // this tile's V has landed
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const unsigned char* vb = vl + 16 * half * RB;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+        const bf16x4 lo = lds_read_tr16(vr);
+        const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
+        o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[half], o[db]);
+      }
+    }
+  };
+
+  // Tile t lives in stage t % NST.  Before tile t is consumed, tile
+  // t + NST - 1 is issued into the stage tile t - 1 used (its reads are done:
+  // their values fed the MFMAs of tile t - 1), so NST - 1 tiles stay in
+  // flight behind the one being consumed.  The last NST - 1 tiles, with
+  // nothing left to issue, wait for everything.
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u)
+    if (u < n_t) issue(u, stage(u));
+  const int n_main = max(0, n_t - (NST - 1));
+  for (int t0 = 0; t0 < n_main; t0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int t = t0 + u;
+      if (t < n_main) {
+        issue(t + NST - 1, stage((u + NST - 1) % NST));
+        consume(t, stage(u), std::integral_constant<int, NST - 1>{});
+      }
+    }
+  }
+  for (int t = n_main; t < n_t; ++t) {
+    wait_vmem();
+    consume(t, stage(t % NST), std::integral_constant<int, 0>{});
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const size_t prow = ((size_t)bkv * p.S + s) * p.R + r;
+    float* po = p.part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        *(f32x4*)(po + col) = f32x4{o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
+                                    o[db][4 * a + 3] * inv};
+      }
+    if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + fast_log2(l_tot) : -INFINITY;
+  }
+}
+
+// One workgroup per query row: merge the row's non-empty chunks.
+template <int D>
+__global__ __launch_bounds__(256) void kv_combine_kernel(KvParams p) {
+  constexpr int TPS = D / 4;      // threads per chunk row (4 floats each)
+  constexpr int SG = 256 / TPS;   // chunks read side by side
+  __shared__ float sacc[SG][D];
+  __shared__ float stot[SG];
+  const int tid = threadIdx.x, dc = tid % TPS, sg = tid / TPS;
+  const int bkv = blockIdx.x / p.R, r = blockIdx.x - bkv * p.R;
+  const int b = bkv / p.H_kv, kvh = bkv - b * p.H_kv;
+  const int gi = r / p.Nq, qi = r - gi * p.Nq;
+  const size_t orow = ((size_t)b * p.H + kvh * p.G + gi) * p.Nq + qi;
+  const int L = cache_len(p, b);
+  const int n_act = min(p.S, (L + p.chunk - 1) / p.chunk);
+  const float* pl = p.part_lse + (size_t)bkv * p.S * p.R + r;
+  const float* po = p.part_o + ((size_t)bkv * p.S * p.R + r) * D + dc * 4;
+
+  float mx = -INFINITY;
+  for (int s = 0; s < n_act; ++s) mx = fmaxf(mx, pl[(size_t)s * p.R]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = sg; s < n_act; s += SG) {
+      const float w = fast_exp2(pl[(size_t)s * p.R] - mx);
+      const f32x4 x = *(const f32x4*)(po + (size_t)s * p.R * D);
+      tot += w;
+      acc += w * x;
+    }
+  }
+  *(f32x4*)&sacc[sg][dc * 4] = acc;
+  if (dc == 0) stot[sg] = tot;
+  __syncthreads();
+  if (sg == 0) {
+    float t = 0.f;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < SG; ++j) {
+      t += stot[j];
+      sum += *(const f32x4*)&sacc[j][dc * 4];
+    }
+    const float inv = t > 0.f ? 1.f / t : 0.f;
+    bf16* out = (bf16*)p.o + orow * D + dc * 4;
+    *(i32x2*)out = i32x2{(int)pack_bf16(sum[0] * inv, sum[1] * inv), (int)pack_bf16(sum[2] * inv, sum[3] * inv)};
+    if (p.lse && dc == 0) p.lse[orow] = t > 0.f ? (mx + fast_log2(t)) * kLn2 : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------- host -------
+// Splits: enough chunks that every CU holds a full complement of waves (one
+// pass, 256 CUs of MI355X), each chunk at least kMinTiles tiles so the
+// partial results stay a small fraction of the cache traffic.
+KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d) {
+  KvPlan pl{};
+  int nw = 0, nst = 0;
+  switch (d) {
+    case 64: nw = KvCfg<64>::NW; nst = KvCfg<64>::NST; break;
+    case 128: nw = KvCfg<128>::NW; nst = KvCfg<128>::NST; break;
+    case 256: nw = KvCfg<256>::NW; nst = KvCfg<256>::NST; break;
+    default: return pl;
+  }
+  constexpr int kCUs = 256, kLds = 160 * 1024, kMinTiles = FA_KV_MIN_TILES, kBC = 32;
+  const long long wg_lds = (long long)nw * nst * 2 * kBC * d * 2;
+  const long long waves_per_cu = (kLds / wg_lds) * nw;
+  pl.G = H / H_kv;
+  pl.R = pl.G * Nq;
+  pl.n_rg = (pl.R + 31) / 32;
+  const long long units = (long long)B * H_kv * pl.n_rg;
+  const long long tiles = (Nkv + kBC - 1) / kBC;
+  const long long s0 = (FA_KV_OVERSUB * kCUs * waves_per_cu + units - 1) / units;
+  long long tps = (tiles + s0 - 1) / s0;
+  if (tps < kMinTiles) tps = kMinTiles;
+  long long S = (tiles + tps - 1) / tps;
+  S = (S + nw - 1) / nw * nw;
+  pl.S = (int)S;
+  pl.chunk = (int)(tps * kBC);
+  pl.nw = nw;
+  const size_t rows = (size_t)B * H_kv * S * pl.R;
+  pl.lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+  pl.ws_bytes = pl.lse_bytes + rows * d * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_kvcache_bf16(int d, bool causal, KvParams& p, hipStream_t s) {
+  const unsigned split_blocks = (unsigned)((size_t)p.B * p.H_kv * p.n_rg * (p.S / p.nw));
+  const unsigned rows = (unsigned)((size_t)p.B * p.H_kv * p.R);
+  auto run = [&](auto dc, auto cc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr bool C = decltype(cc)::value;
+    hipLaunchKernelGGL((kv_split_kernel<D, C>), dim3(split_blocks), dim3(KvCfg<D>::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((kv_combine_kernel<D>), dim3(rows), dim3(256), 0, s, p);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  switch (d) {
+    case 64: causal ? run(std::integral_constant<int, 64>{}, T{}) : run(std::integral_constant<int, 64>{}, F{}); break;
+    case 128: causal ? run(std::integral_constant<int, 128>{}, T{}) : run(std::integral_constant<int, 128>{}, F{}); break;
+    case 256: causal ? run(std::integral_constant<int, 256>{}, T{}) : run(std::integral_constant<int, 256>{}, F{}); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

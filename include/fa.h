@@ -109,8 +109,47 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
                  int causal, fa_dtype dtype, hipStream_t stream);
 
+/*
+ * Bytes of device workspace fa_fwd_kvcache needs for this problem (0 on
+ * invalid arguments or an unsupported (dtype, d)).  A pure function of its
+ * arguments.
+ */
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d,
+                                      fa_dtype dtype);
+
+/*
+ * Forward pass of N_q new queries against a KV cache (decode).  In decode the
+ * query side is a single token (or a few) and the cost moves to reading the
+ * cache; the read is split over many workgroups, as "FlashAttentionとは？…"
+ * describes for FA2's KV-cache entry point (section 短い系列の効果とデコード
+ * 向け最適化の違い), and the per-chunk results are merged with their
+ * logsumexps by a second kernel.
+ *   Q [B][H][N_q][d]; K_cache, V_cache [B][H_kv][N_kv][d] (N_kv is the cache
+ *   capacity; GQA as in fa_fwd); O [B][H][N_q][d] bf16; LSE [B][H][N_q] fp32
+ *   or NULL.
+ *   kv_len: DEVICE int32 [B], the number of cache rows batch b uses, or NULL
+ *     for N_kv everywhere.  Values are clamped to [0, N_kv] on the device
+ *     (they cannot be checked on the host without a synchronisation).
+ *   The N_q queries are the last N_q positions of each sequence: with
+ *   causal != 0, query i of batch b sees keys 0 .. kv_len[b] - N_q + i
+ *   (bottom-right alignment); otherwise all kv_len[b] keys.  A query row that
+ *   sees no key gets O = 0 and LSE = -inf.
+ *   workspace: caller-owned device memory of at least
+ *   fa_fwd_kvcache_workspace_bytes(...) bytes, 256-byte aligned; contents on
+ *   entry do not matter and are garbage on return.
+ * Supported: BF16 with d = 64, 128, 256.  Any N_q >= 1, N_kv >= 1; the split
+ * pays off for small N_q (G * N_q <= 32 query rows per K/V head read once).
+ */
+fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache, const int* kv_len,
+                         void* O, float* LSE, void* workspace, size_t workspace_bytes, int B, int H,
+                         int H_kv, int N_q, int N_kv, int d, float scale, int causal, fa_dtype dtype,
+                         hipStream_t stream);
+
 /* 1 if a kernel exists for (dtype, d, backward != 0), else 0. */
 int fa_supported(fa_dtype dtype, int d, int backward);
+
+/* 1 if fa_fwd_kvcache has a kernel for (dtype, d), else 0. */
+int fa_kvcache_supported(fa_dtype dtype, int d);
 
 /* Static, never-NULL description of a status code. */
 const char* fa_status_string(fa_status s);

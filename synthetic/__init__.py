@@ -175,3 +175,80 @@ def rand_rows(n_total: int, count: int, seed: int):
     idx = torch.randperm(n_total, generator=g)[:count]
     idx = torch.unique(torch.cat([idx, torch.tensor([0, n_total - 1])]))
     return idx.tolist()
+
+
+# ------------------------------------------------------- KV-cache (decode) ---
+
+@dataclass(frozen=True)
+class KvCacheWorkload:
+    """N_q new queries per head against a KV cache of capacity N_kv.
+
+    ``ragged``: the cache lengths of the batch are drawn (seeded) in
+    [1, N_kv] instead of all being N_kv.
+    """
+
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    N_q: int
+    N_kv: int
+    d: int
+    dtype: str = "bf16"
+    causal: bool = True
+    amp: float = 1.0
+    seed: int = 0
+    ragged: bool = False
+    note: str = field(default="", compare=False)
+
+    def cache_bytes(self, lens) -> int:
+        """Bytes of K and V a call reads: every used cache row once."""
+        elem = {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+        return 2 * self.H_kv * self.d * elem * int(sum(lens))
+
+    def flops(self, lens) -> float:
+        """4 * d flops per (query, visible key) pair (QK^T and PV)."""
+        tot = 0
+        for n in lens:
+            for i in range(self.N_q):
+                tot += max(0, min(n, n - self.N_q + i + 1)) if self.causal else n
+        return 4.0 * self.H * self.d * tot
+
+
+# One new token per sequence with the GQA head layout of the prefill shape
+# (32 query heads on 8 K/V heads, d = 128) and a 32K-token cache; seeds 10+.
+KV_WORKLOADS = {
+    "D1": KvCacheWorkload("D1", 8, 32, 8, 1, 32768, 128, seed=10,
+                          note="decode, one new token per sequence, full 32K caches"),
+    "D1_ragged": KvCacheWorkload("D1_ragged", 8, 32, 8, 1, 32768, 128, seed=11, ragged=True,
+                                 note="decode with a seeded mix of cache lengths in [1, 32768]"),
+}
+
+
+def draw_kvcache(B, H, H_kv, N_q, N_kv, d, amp=1.0, seed=0):
+    """fp32 N(0, amp^2) draws in the fixed order Q [B,H,N_q,d], K, V [B,H_kv,N_kv,d]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, N_q, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, H_kv, N_kv, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H_kv, N_kv, d, generator=g, dtype=torch.float32)
+    if amp != 1.0:
+        q.mul_(amp)
+        k.mul_(amp)
+        v.mul_(amp)
+    return q, k, v
+
+
+def cache_lengths(B, N_kv, seed):
+    """Seeded cache lengths, uniform in [1, N_kv], as a CPU int32 tensor [B]."""
+    g = torch.Generator("cpu").manual_seed(seed + 7919)
+    return torch.randint(1, N_kv + 1, (B,), generator=g, dtype=torch.int32)
+
+
+def make_kvcache_inputs(w: KvCacheWorkload):
+    """pack_inputs of the workload's draws plus ``kv_len`` (int32 CPU tensor or
+    None) and ``lens`` (the lengths as a list, N_kv each when not ragged)."""
+    q, k, v = draw_kvcache(w.B, w.H, w.H_kv, w.N_q, w.N_kv, w.d, w.amp, w.seed)
+    out = pack_inputs(q, k, v, None, w.dtype)
+    out["kv_len"] = cache_lengths(w.B, w.N_kv, w.seed) if w.ragged else None
+    out["lens"] = out["kv_len"].tolist() if w.ragged else [w.N_kv] * w.B
+    return out

@@ -112,6 +112,48 @@ def test_bwd_validation(lib):
     assert bwd(lib, ptrs=[P * (i + 1) for i in range(8)] + [P]) == 4   # dV aliases Q
 
 
+def kvc(lib, q=P, k=2 * P, v=3 * P, kv_len=None, o=4 * P, lse=5 * P, ws=64 * P, ws_bytes=1 << 30,
+        B=2, H=8, Hkv=2, Nq=1, Nkv=300, d=128, scale=0.08, causal=1, dtype=1):
+    return lib.fa_fwd_kvcache(q, k, v, kv_len, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, scale,
+                              causal, dtype, None)
+
+
+def test_kvcache_validation(lib):
+    assert kvc(lib, q=None) == 1
+    assert kvc(lib, o=None) == 1
+    assert kvc(lib, Nq=0) == 2
+    assert kvc(lib, Nkv=0) == 2
+    assert kvc(lib, Hkv=3) == 2                      # H not a multiple of H_kv
+    assert kvc(lib, d=96) == 3
+    assert kvc(lib, dtype=0, d=64) == 3              # no fp32 decode kernel
+    assert kvc(lib, dtype=2) == 3
+    assert kvc(lib, scale=0.0) == 4
+    assert kvc(lib, scale=float("inf")) == 4
+    assert kvc(lib, kv_len=6 * P + 2) == 4           # kv_len not 4-byte aligned
+    assert kvc(lib, o=P + 16) == 4                   # O overlaps Q
+    assert kvc(lib, kv_len=4 * P) == 4               # O overlaps kv_len
+    assert kvc(lib, ws=None) == 5
+    assert kvc(lib, ws_bytes=1024) == 5
+    assert kvc(lib, ws=64 * P + 16) == 5             # workspace not 256-byte aligned
+    assert kvc(lib, ws=4 * P) == 4                   # workspace overlaps O
+
+
+def test_kvcache_workspace_bytes(lib):
+    for d in (64, 128, 256):
+        assert fa.fa_kvcache_supported(1, d)
+    assert not fa.fa_kvcache_supported(1, 96) and not fa.fa_kvcache_supported(0, 64)
+    assert fa.fa_fwd_kvcache_workspace_bytes(1, 8, 2, 1, 300, 96) == 0
+    assert fa.fa_fwd_kvcache_workspace_bytes(1, 8, 3, 1, 300, 128) == 0
+    # a chunk holds at least 4 tiles of 32 keys, so a 300-row cache splits in
+    # ceil(10/4) = 3 chunks, rounded up to a multiple of the waves per workgroup
+    ws = fa.fa_fwd_kvcache_workspace_bytes(1, 8, 2, 1, 300, 128)
+    rows = 1 * 2 * 4 * 4                             # B * H_kv * S * (G * N_q)
+    assert ws == ((rows * 4 + 255) // 256) * 256 + rows * 128 * 4
+    # the workspace grows with the chunks, never with the cache itself
+    big = fa.fa_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128)
+    assert 0 < big < 8 * 8 * 32768 * 128 * 2 // 16
+
+
 def test_workspace_bytes(lib):
     assert fa.fa_bwd_workspace_bytes(2, 16, 16, 16384, 64) == 2 * (2 * 16 * 16384 * 4)
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 512
