@@ -161,7 +161,8 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv,
                                       fa_dtype dtype) {
   if (!valid_dtype(dtype) || !fa_kvcache_supported(dtype, d)) return 0;
   if (check_shape(B, H, H_kv, N_q, d) != FA_OK || check_shape(B, H_kv, H_kv, N_kv, d) != FA_OK) return 0;
-  return fa::kv_plan(B, H, H_kv, N_q, N_kv, d).ws_bytes;
+  const fa::KvPlan plan = fa::kv_plan(B, H, H_kv, N_q, N_kv, d);
+  return plan.max_tiles > 0x7fffffffll || plan.W > 0x7fffffffll ? 0 : plan.ws_bytes;
 }
 
 fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache, const int* kv_len,
@@ -180,6 +181,8 @@ fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache
       (reinterpret_cast<uintptr_t>(kv_len) & 3u))
     return FA_ERR_INVALID_VALUE;
   const fa::KvPlan plan = fa::kv_plan(B, H, H_kv, N_q, N_kv, d);
+  // tile and wave indices are 32-bit
+  if (plan.max_tiles > 0x7fffffffll || plan.W > 0x7fffffffll) return FA_ERR_INVALID_SHAPE;
   if (!workspace || workspace_bytes < plan.ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return FA_ERR_WORKSPACE;
   const size_t eb = elem_bytes(dtype);
@@ -202,8 +205,9 @@ fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache
   p.part_lse = (float*)workspace;
   p.part_o = (float*)((char*)workspace + plan.lse_bytes);
   p.B = B; p.H = H; p.H_kv = H_kv; p.Nq = N_q; p.Nkv = N_kv;
-  p.G = plan.G; p.R = plan.R; p.n_rg = plan.n_rg;
-  p.S = plan.S; p.chunk = plan.chunk; p.nw = plan.nw;
+  p.G = plan.G; p.R = plan.R; p.n_rg = plan.n_rg; p.R_pad = plan.R_pad;
+  p.upb = H_kv * plan.n_rg;
+  p.W = (int)plan.W; p.nw = plan.nw;
   p.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_kvcache_bf16(d, causal != 0, p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -50,19 +50,22 @@ struct KvParams {
   const int* kv_len;   // [B] rows of the cache in use, or null (all Nkv)
   void* o;             // [B][H][Nq][d]
   float* lse;          // [B][H][Nq] or null
-  float* part_lse;     // workspace: [B*H_kv][S][R] chunk logsumexp (base 2, scaled)
-  float* part_o;       // workspace: [B*H_kv][S][R][d] chunk outputs (normalised)
+  float* part_lse;     // workspace: [W][R_pad] partial logsumexp per wave (base 2, scaled)
+  float* part_o;       // workspace: [W][R_pad][d] partial outputs per wave (normalised)
   int B, H, H_kv, Nq, Nkv;
-  int G, R, n_rg;      // heads per group, rows per group (G*Nq), 32-row groups
-  int S, chunk, nw;    // chunks per group, keys per chunk, waves per workgroup
+  int G, R, n_rg, R_pad; // heads per group, rows per group (G*Nq), 32-row groups, min(R, 32)
+  int upb;             // units per batch: H_kv * n_rg
+  int W, nw;           // waves of the split grid, waves per workgroup
   float scale_log2;
 };
 
-// Chunking of a KV-cache problem: a pure function of the shape.
+// Launch shape and workspace of a KV-cache problem: a pure function of the shape.
 struct KvPlan {
-  int G, R, n_rg, S, chunk, nw;
+  int G, R, n_rg, R_pad, nw;
+  long long W;         // waves of the split grid
   size_t lse_bytes;    // offset of part_o in the workspace (256-aligned)
   size_t ws_bytes;     // total workspace
+  long long max_tiles; // 32-key tiles of the whole problem at full caches
 };
 KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d);
 

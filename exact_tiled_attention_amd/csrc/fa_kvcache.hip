@@ -57,12 +57,9 @@ namespace fa {
 #define FA_KV_NST256 2
 #endif
 
-// Chunks per resident wave slot, and the smallest chunk (in 32-key tiles).
-#ifndef FA_KV_OVERSUB
-#define FA_KV_OVERSUB 1
-#endif
+// Fewest 32-key tiles a wave is given (small problems use fewer waves).
 #ifndef FA_KV_MIN_TILES
-#define FA_KV_MIN_TILES 4
+#define FA_KV_MIN_TILES 2
 #endif
 
 template <int D>
@@ -90,6 +87,99 @@ __device__ __forceinline__ int cache_len(const KvParams& p, int b) {
   return p.kv_len ? min(max(p.kv_len[b], 0), p.Nkv) : p.Nkv;
 }
 
+// ---------------------------------------------------------- work split -----
+// A unit is (batch, K/V head, 32-row query group); batch b's units each hold
+// t_b = ceil(len_b / 32) tiles of 32 keys, T tiles in all.  Of the W waves
+// launched (at least one per unit), each unit gets one, and the E = W - U
+// others are shared out in proportion to tiles: a unit of batch b is cut
+// into n_b = 1 + floor(t_b E / T) near-equal pieces, one per wave.  The
+// pieces of all units are then about T / E tiles whatever the mix of cache
+// lengths, so a ragged batch keeps every CU busy.  The lengths live on the
+// device; every wave and the combine derive the same partition from them.
+__device__ __forceinline__ int batch_tiles(const KvParams& p, int b) {
+  return (cache_len(p, b) + 31) >> 5;
+}
+// Wave-wide inclusive prefix sum of one int per lane.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+struct KvSplit {
+  int total;   // T: tiles of all units
+  int extra;   // E: waves beyond one per unit
+};
+__device__ __forceinline__ KvSplit kv_split(const KvParams& p) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  if (!p.kv_len) {                             // every cache full: no scan
+    KvSplit sp;
+    sp.total = p.B * p.upb * ((p.Nkv + 31) >> 5);
+    sp.extra = min(p.W - p.B * p.upb, sp.total / FA_KV_MIN_TILES);
+    return sp;
+  }
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    int v = b < p.B ? batch_tiles(p, b) * p.upb : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    total += v;
+  }
+  // the same in every lane; readfirstlane lets the compiler keep it in an SGPR
+  KvSplit sp;
+  sp.total = __builtin_amdgcn_readfirstlane(total);
+  sp.extra = min(p.W - p.B * p.upb, sp.total / FA_KV_MIN_TILES);
+  return sp;
+}
+__device__ __forceinline__ int pieces_of(const KvSplit& sp, int tiles) {
+  return sp.total > 0 ? 1 + (int)((long long)tiles * sp.extra / sp.total) : 1;
+}
+// Batch of wave w and the first wave of that batch; bt = B when w is past
+// the last batch's waves.
+__device__ __forceinline__ void wave_batch(const KvParams& p, const KvSplit& sp, int w, int& bt, int& first) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  bt = p.B;
+  first = 0;
+  if (!p.kv_len) {
+    const int per = pieces_of(sp, (p.Nkv + 31) >> 5) * p.upb;
+    bt = min(w / per, p.B);
+    first = bt * per;
+    return;
+  }
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < p.B ? pieces_of(sp, batch_tiles(p, b)) * p.upb : 0;
+    const int incl = wave_incl_scan(v);
+    const unsigned long long hit = __ballot(b < p.B && base + incl - v <= w && w < base + incl);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      bt = b0 + l;
+      first = base + __shfl(incl - v, l, 64);
+      return;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+}
+// First wave of batch bt.
+__device__ __forceinline__ int batch_first_wave(const KvParams& p, const KvSplit& sp, int bt) {
+  const int lane = threadIdx.x & 63;
+  int base = 0, first = 0;
+  if (!p.kv_len) return bt * pieces_of(sp, (p.Nkv + 31) >> 5) * p.upb;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < p.B ? pieces_of(sp, batch_tiles(p, b)) * p.upb : 0;
+    const int incl = wave_incl_scan(v);
+    if (bt >= b0 && bt < b0 + 64) first = base + __shfl(incl - v, bt - b0, 64);
+    base += __shfl(incl, 63, 64);
+  }
+  return first;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(KvCfg<D>::NW * 64) void kv_split_kernel(KvParams p) {
   using T = KvTile<D>;
@@ -103,43 +193,24 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64) void kv_split_kernel(KvParams p)
 
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lr = lane & 31, g = lane >> 5;
-  // block -> (b * H_kv + kv head, workgroup split, row group)
-  const int wg_per = p.S / NW;
-  const int rg = blockIdx.x % p.n_rg;
-  const int rest = blockIdx.x / p.n_rg;
-  const int wgs = rest % wg_per;
-  const int bkv = rest / wg_per;
-  const int b = bkv / p.H_kv, kvh = bkv - b * p.H_kv;
-  const int s = wgs * NW + wid;              // this wave's chunk
+  const int w = blockIdx.x * NW + wid;
+  const KvSplit sp = kv_split(p);
+  int b, first;
+  wave_batch(p, sp, w, b, first);
+  // wave-uniform values: in SGPRs the buffer descriptors built from them need
+  // no per-lane (waterfall) handling
+  b = __builtin_amdgcn_readfirstlane(b);
+  first = __builtin_amdgcn_readfirstlane(first);
+  if (b >= p.B) return;                      // a wave past the last piece
   const int L = cache_len(p, b);
-  const int k_begin = s * p.chunk;
-  if (k_begin >= L) return;                  // empty chunk: the combine skips it
-  const int k_end = min(L, k_begin + p.chunk);
-  const int n_t = (k_end - k_begin + BC - 1) / BC;
+  const int tb = (L + 31) >> 5;
+  const int nb = pieces_of(sp, tb);
+  const int j = (w - first) / nb;            // unit within the batch
+  const int piece = w - first - j * nb;
+  const int lo = (int)((long long)piece * tb / nb), hi = (int)((long long)(piece + 1) * tb / nb);
+  if (lo >= hi) return;                      // an empty piece: the combine skips it
 
-  // This lane's query row; lanes past the group's rows compute on zeros.
-  const int r = rg * 32 + lr;
-  const bool row_ok = r < p.R;
-  const int gi = row_ok ? r / p.Nq : 0;
-  const int qi = row_ok ? r - gi * p.Nq : p.Nq - 1;
-  const int h = kvh * p.G + gi;
-  // last visible key of the row, and the smallest one over the group
-  const int lim = CAUSAL ? min(L - p.Nq + qi, L - 1) : L - 1;
-  const int lim_lo = CAUSAL ? L - p.Nq : L - 1;
-
-  bf16x8 qr[D / 16];
-  {
-    const unsigned char* qrow = (const unsigned char*)p.q + (((size_t)b * p.H + h) * p.Nq + qi) * RB;
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      bf16x8 x = {};
-      if (row_ok) x = *(const bf16x8*)(qrow + (kb * 16 + 8 * g) * 2);
-      qr[kb] = x;
-    }
-  }
-
-  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * p.Nkv * RB;
-  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * p.Nkv * RB;
+  // Per-lane LDS offsets, fixed for every tile.
   int dma_k[IPT], dma_v[IPT];
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
@@ -158,193 +229,248 @@ __global__ __launch_bounds__(KvCfg<D>::NW * 64) void kv_split_kernel(KvParams p)
 #pragma unroll
   for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G4 & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
-
   auto stage = [&](int u) -> unsigned char* {
-    unsigned char* base = u == 0 ? st0 : (u == 1 ? st1 : (u == 2 ? st2 : st3));
+    unsigned char* base = u == 0 ? st0 : (NST == 2 || u == 1 ? st1 : (NST == 3 || u == 2 ? st2 : st3));
     return base + wid * T::STAGE;
   };
-  auto issue = [&](int t, unsigned char* st) {
-    const int key0 = k_begin + t * BC;
-    const int bytes = min(L - key0, BC) * RB;   // rows past the cache length read as zero
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) dma16_buf_nt(rk, dma_k[i], st + i * 1024);
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) dma16_buf_nt(rv, dma_v[i], st + T::TILE + i * 1024);
-  };
-
   const float c = p.scale_log2;
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
 
-  // LATER = tiles issued after this one; their DMAs may stay in flight.
-  auto consume = [&](int t, const unsigned char* kl, auto later_c) __attribute__((always_inline)) {
-    constexpr int LATER = decltype(later_c)::value;
-    const unsigned char* vl = kl + T::TILE;
-    const int key0 = k_begin + t * BC;
-    wait_vmem_upto<LATER * 2 * IPT + IPT>();          // this tile's K has landed
-    f32x16 sc = {};
+  // This wave's piece: tiles [lo, hi) of unit j (= kv head * n_rg + row
+  // group) of batch b; its result goes to partial slot w.
+  {
+    const int kvh = j / p.n_rg, rg = j - kvh * p.n_rg;
+    const int bkv = b * p.H_kv + kvh;
+    const int k_begin = lo * BC;
+    const int n_t = hi - lo;
+
+    // This lane's query row; lanes past the group's rows compute on zeros.
+    const int r = rg * 32 + lr;
+    const bool row_ok = r < p.R;
+    const int gi = row_ok ? r / p.Nq : 0;
+    const int qi = row_ok ? r - gi * p.Nq : p.Nq - 1;
+    const int h = kvh * p.G + gi;
+    // last visible key of the row, and the smallest one over the group
+    const int lim = CAUSAL ? min(L - p.Nq + qi, L - 1) : L - 1;
+    const int lim_lo = CAUSAL ? L - p.Nq : L - 1;
+
+    bf16x8 qr[D / 16];
+    {
+      const unsigned char* qrow = (const unsigned char*)p.q + (((size_t)b * p.H + h) * p.Nq + qi) * RB;
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      const bf16x8 a = *(const bf16x8*)(kl + (kb / NKO) * 256 + koff[kb % NKO]);
-      sc = mfma_bf16(a, qr[kb], sc);
-    }
-    if (key0 + BC - 1 > lim_lo) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int key = key0 + 8 * (q >> 2) + 4 * g + (q & 3);
-        if (key > lim) sc[q] = -INFINITY;
+      for (int kb = 0; kb < D / 16; ++kb) {
+        bf16x8 x = {};
+        if (row_ok) x = *(const bf16x8*)(qrow + (kb * 16 + 8 * g) * 2);
+        qr[kb] = x;
       }
     }
-    // P against the running max; the max is taken (and the output rescaled)
-    // only when some lane's partial sum leaves [0, kSumBound], which also
-    // catches rows that have not seen a key yet (running max -inf).
-    bf16x8 pk[2];
-    auto expo = [&](float m) __attribute__((always_inline)) -> float {
-      float tsum = 0.f;
+    const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * p.Nkv * RB;
+    const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * p.Nkv * RB;
+    auto issue = [&](int t, unsigned char* st) {
+      const int key0 = k_begin + t * BC;
+      const int bytes = min(L - key0, BC) * RB;   // rows past the cache length read as zero
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) dma16_buf_nt(rk, dma_k[i], st + i * 1024);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) dma16_buf_nt(rv, dma_v[i], st + T::TILE + i * 1024);
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // LATER = tiles issued after this one; their DMAs may stay in flight.
+    auto consume = [&](int t, const unsigned char* kl, auto later_c) __attribute__((always_inline)) {
+      constexpr int LATER = decltype(later_c)::value;
+      const unsigned char* vl = kl + T::TILE;
+      const int key0 = k_begin + t * BC;
+      wait_vmem_upto<LATER * 2 * IPT + IPT>();          // this tile's K has landed
+      f32x16 sc = {};
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kl + (kb / NKO) * 256 + koff[kb % NKO]);
+        sc = mfma_bf16(a, qr[kb], sc);
+      }
+      if (key0 + BC - 1 > lim_lo) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int key = key0 + 8 * (q >> 2) + 4 * g + (q & 3);
+          if (key > lim) sc[q] = -INFINITY;
+        }
+      }
+      // P against the running max; the max is taken (and the output
+      // rescaled) only when some lane's partial sum leaves [0, kSumBound],
+      // which also catches rows that have not seen a key yet (max -inf).
+      bf16x8 pk[2];
+      auto expo = [&](float m) __attribute__((always_inline)) -> float {
+        float tsum = 0.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float e0 = fast_exp2(fmaf(sc[half * 8 + 2 * x], c, -m));
+            const float e1 = fast_exp2(fmaf(sc[half * 8 + 2 * x + 1], c, -m));
+            w4[x] = pack_bf16(e0, e1);
+            tsum += e0 + e1;
+          }
+          pk[half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+        return tsum;
+      };
+      float ts = expo(m_run);
+      if (__any(!(ts <= kSumBound))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sc[q]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m_run, mx * c);
+        // A row with no visible key so far keeps m = -inf, l = 0, O = 0; its
+        // exponentials are then taken against 0 so that masked scores give 0.
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) o[i][q] *= alpha;
+        ts = expo(none ? 0.f : m_new);
+      }
+      l_run += ts;
+      wait_vmem_upto<LATER * 2 * IPT>();                // this tile's V has landed
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        uint32_t w4[4];
+        const unsigned char* vb = vl + 16 * half * RB;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(fmaf(sc[half * 8 + 2 * w], c, -m));
-          const float e1 = fast_exp2(fmaf(sc[half * 8 + 2 * w + 1], c, -m));
-          w4[w] = pack_bf16(e0, e1);
-          tsum += e0 + e1;
+        for (int db = 0; db < D / 32; ++db) {
+          const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+          const bf16x4 lo4 = lds_read_tr16(vr);
+          const bf16x4 hi4 = lds_read_tr16(vr + 8 * RB);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pk[half], o[db]);
         }
-        pk[half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
       }
-      return tsum;
     };
-    float ts = expo(m_run);
-    if (__any(!(ts <= kSumBound))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sc[q]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      // A row with no visible key so far keeps m = -inf, l = 0, O = 0; its
-      // exponentials are then taken against 0 so that masked scores give 0.
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) o[i][q] *= alpha;
-      ts = expo(none ? 0.f : m_new);
-    }
-    l_run += ts;
-    wait_vmem_upto<LATER * 2 * IPT>();                // this tile's V has landed
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const unsigned char* vb = vl + 16 * half * RB;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
-        const bf16x4 lo = lds_read_tr16(vr);
-        const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
-        o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[half], o[db]);
-      }
-    }
-  };
 
-  // Tile t lives in stage t % NST.  Before tile t is consumed, tile
-  // t + NST - 1 is issued into the stage tile t - 1 used (its reads are done:
-  // their values fed the MFMAs of tile t - 1), so NST - 1 tiles stay in
-  // flight behind the one being consumed.  The last NST - 1 tiles, with
-  // nothing left to issue, wait for everything.
+    // Tile t lives in stage t % NST.  Before tile t is consumed, tile
+    // t + NST - 1 is issued into the stage tile t - 1 used (its reads are
+    // done: their values fed the MFMAs of tile t - 1), so NST - 1 tiles stay
+    // in flight behind the one being consumed.  The last NST - 1 tiles, with
+    // nothing left to issue, wait for everything.
 #pragma unroll
-  for (int u = 0; u < NST - 1; ++u)
-    if (u < n_t) issue(u, stage(u));
-  const int n_main = max(0, n_t - (NST - 1));
-  for (int t0 = 0; t0 < n_main; t0 += NST) {
+    for (int u = 0; u < NST - 1; ++u)
+      if (u < n_t) issue(u, stage(u));
+    const int n_main = max(0, n_t - (NST - 1));
+    for (int t0 = 0; t0 < n_main; t0 += NST) {
 #pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int t = t0 + u;
-      if (t < n_main) {
-        issue(t + NST - 1, stage((u + NST - 1) % NST));
-        consume(t, stage(u), std::integral_constant<int, NST - 1>{});
+      for (int u = 0; u < NST; ++u) {
+        const int t = t0 + u;
+        if (t < n_main) {
+          issue(t + NST - 1, stage((u + NST - 1) % NST));
+          consume(t, stage(u), std::integral_constant<int, NST - 1>{});
+        }
       }
     }
-  }
-  for (int t = n_main; t < n_t; ++t) {
-    wait_vmem();
-    consume(t, stage(t % NST), std::integral_constant<int, 0>{});
+    for (int t = n_main; t < n_t; ++t) {
+      wait_vmem();
+      consume(t, stage(t % NST), std::integral_constant<int, 0>{});
+    }
+
+    const float l_tot = sum_halves(l_run);
+    if (row_ok) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const size_t prow = (size_t)w * p.R_pad + lr;
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int col = db * 32 + 8 * a + 4 * g;
+          *(f32x4*)(po + col) = f32x4{o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
+                                      o[db][4 * a + 3] * inv};
+        }
+      if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + fast_log2(l_tot) : -INFINITY;
+    }
   }
 
-  const float l_tot = sum_halves(l_run);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const size_t prow = ((size_t)bkv * p.S + s) * p.R + r;
-    float* po = p.part_o + prow * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = db * 32 + 8 * a + 4 * g;
-        *(f32x4*)(po + col) = f32x4{o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
-                                    o[db][4 * a + 3] * inv};
-      }
-    if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + fast_log2(l_tot) : -INFINITY;
-  }
 }
 
-// One workgroup per query row: merge the row's non-empty chunks.
+// One workgroup per query row: merge the partials of the row's unit, which
+// are the consecutive waves that took its pieces.
 template <int D>
 __global__ __launch_bounds__(256) void kv_combine_kernel(KvParams p) {
-  constexpr int TPS = D / 4;      // threads per chunk row (4 floats each)
-  constexpr int SG = 256 / TPS;   // chunks read side by side
+  constexpr int TPS = D / 4;      // threads per partial row (4 floats each)
+  constexpr int SG = 256 / TPS;   // partials read side by side
   __shared__ float sacc[SG][D];
   __shared__ float stot[SG];
+  __shared__ float smx[SG];
   const int tid = threadIdx.x, dc = tid % TPS, sg = tid / TPS;
   const int bkv = blockIdx.x / p.R, r = blockIdx.x - bkv * p.R;
   const int b = bkv / p.H_kv, kvh = bkv - b * p.H_kv;
   const int gi = r / p.Nq, qi = r - gi * p.Nq;
+  const int rg = r >> 5, rr = r & 31;
+  const int j = kvh * p.n_rg + rg;
   const size_t orow = ((size_t)b * p.H + kvh * p.G + gi) * p.Nq + qi;
-  const int L = cache_len(p, b);
-  const int n_act = min(p.S, (L + p.chunk - 1) / p.chunk);
-  const float* pl = p.part_lse + (size_t)bkv * p.S * p.R + r;
-  const float* po = p.part_o + ((size_t)bkv * p.S * p.R + r) * D + dc * 4;
 
-  float mx = -INFINITY;
-  for (int s = 0; s < n_act; ++s) mx = fmaxf(mx, pl[(size_t)s * p.R]);
+  const KvSplit sp = kv_split(p);
+  const int tb = batch_tiles(p, b);
+  const int nb = pieces_of(sp, tb);
+  // pieces [lo, hi) with lo < hi hold tiles; with nb <= tb every piece does
+  const int n_part = tb == 0 ? 0 : min(nb, tb);
+  const size_t slot0 = (size_t)batch_first_wave(p, sp, b) + (size_t)j * nb;
+  const float* pl = p.part_lse + slot0 * p.R_pad + rr;
+  const float* po = p.part_o + (slot0 * p.R_pad + rr) * D + dc * 4;
+  const size_t stride = (size_t)p.R_pad;         // rows between consecutive slots
+
+  // One pass: each thread merges its partials online (running max m, sum of
+  // weights t, weighted output acc), then the SG groups merge through LDS.
+  float m = -INFINITY, t = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = sg; s < n_act; s += SG) {
-      const float w = fast_exp2(pl[(size_t)s * p.R] - mx);
-      const f32x4 x = *(const f32x4*)(po + (size_t)s * p.R * D);
-      tot += w;
-      acc += w * x;
-    }
+  // (a piece whose rows saw no key has l = -inf and x = 0; while every piece
+  // so far is such, mn stays -inf and nothing accumulates)
+#pragma unroll 4
+  for (int s = sg; s < n_part; s += SG) {
+    const float l = pl[s * stride];
+    const f32x4 x = *(const f32x4*)(po + s * stride * D);
+    const float mn = fmaxf(m, l);
+    const bool none = mn == -INFINITY;
+    const float a = none ? 1.f : fast_exp2(m - mn), wgt = none ? 0.f : fast_exp2(l - mn);
+    acc = acc * a + x * wgt;
+    t = t * a + wgt;
+    m = mn;
   }
   *(f32x4*)&sacc[sg][dc * 4] = acc;
-  if (dc == 0) stot[sg] = tot;
+  if (dc == 0) {
+    stot[sg] = t;
+    smx[sg] = m;
+  }
   __syncthreads();
   if (sg == 0) {
-    float t = 0.f;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < SG; ++j) {
-      t += stot[j];
-      sum += *(const f32x4*)&sacc[j][dc * 4];
+    for (int q = 0; q < SG; ++q) mx = fmaxf(mx, smx[q]);
+    float tt = 0.f;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < SG; ++q) {
+        const float a = fast_exp2(smx[q] - mx);
+        tt += stot[q] * a;
+        sum += *(const f32x4*)&sacc[q][dc * 4] * a;
+      }
     }
-    const float inv = t > 0.f ? 1.f / t : 0.f;
+    const float inv = tt > 0.f ? 1.f / tt : 0.f;
     bf16* out = (bf16*)p.o + orow * D + dc * 4;
     *(i32x2*)out = i32x2{(int)pack_bf16(sum[0] * inv, sum[1] * inv), (int)pack_bf16(sum[2] * inv, sum[3] * inv)};
-    if (p.lse && dc == 0) p.lse[orow] = t > 0.f ? (mx + fast_log2(t)) * kLn2 : -INFINITY;
+    if (p.lse && dc == 0) p.lse[orow] = tt > 0.f ? (mx + fast_log2(tt)) * kLn2 : -INFINITY;
   }
 }
 
 // ------------------------------------------------------------- host -------
-// Splits: enough chunks that every CU holds a full complement of waves (one
-// pass, 256 CUs of MI355X), each chunk at least kMinTiles tiles so the
-// partial results stay a small fraction of the cache traffic.
+// Waves: one pass of the chip (every resident wave slot of the 256 CUs of
+// MI355X), and at least one per unit; one partial slot per wave.
 KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d) {
   KvPlan pl{};
   int nw = 0, nst = 0;
@@ -354,30 +480,26 @@ KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d) {
     case 256: nw = KvCfg<256>::NW; nst = KvCfg<256>::NST; break;
     default: return pl;
   }
-  constexpr int kCUs = 256, kLds = 160 * 1024, kMinTiles = FA_KV_MIN_TILES, kBC = 32;
+  constexpr int kCUs = 256, kLds = 160 * 1024, kBC = 32;
   const long long wg_lds = (long long)nw * nst * 2 * kBC * d * 2;
-  const long long waves_per_cu = (kLds / wg_lds) * nw;
+  pl.nw = nw;
   pl.G = H / H_kv;
   pl.R = pl.G * Nq;
   pl.n_rg = (pl.R + 31) / 32;
+  pl.R_pad = pl.R < 32 ? pl.R : 32;
   const long long units = (long long)B * H_kv * pl.n_rg;
-  const long long tiles = (Nkv + kBC - 1) / kBC;
-  const long long s0 = (FA_KV_OVERSUB * kCUs * waves_per_cu + units - 1) / units;
-  long long tps = (tiles + s0 - 1) / s0;
-  if (tps < kMinTiles) tps = kMinTiles;
-  long long S = (tiles + tps - 1) / tps;
-  S = (S + nw - 1) / nw * nw;
-  pl.S = (int)S;
-  pl.chunk = (int)(tps * kBC);
-  pl.nw = nw;
-  const size_t rows = (size_t)B * H_kv * S * pl.R;
+  long long W = kCUs * (kLds / wg_lds) * nw;
+  if (W < units) W = (units + nw - 1) / nw * nw;
+  pl.W = W;
+  pl.max_tiles = units * ((Nkv + kBC - 1) / kBC);
+  const size_t rows = (size_t)W * pl.R_pad;
   pl.lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
   pl.ws_bytes = pl.lse_bytes + rows * d * sizeof(float);
   return pl;
 }
 
 hipError_t launch_kvcache_bf16(int d, bool causal, KvParams& p, hipStream_t s) {
-  const unsigned split_blocks = (unsigned)((size_t)p.B * p.H_kv * p.n_rg * (p.S / p.nw));
+  const unsigned split_blocks = (unsigned)(p.W / p.nw);
   const unsigned rows = (unsigned)((size_t)p.B * p.H_kv * p.R);
   auto run = [&](auto dc, auto cc) {
     constexpr int D = decltype(dc)::value;

@@ -144,14 +144,16 @@ def test_kvcache_workspace_bytes(lib):
     assert not fa.fa_kvcache_supported(1, 96) and not fa.fa_kvcache_supported(0, 64)
     assert fa.fa_fwd_kvcache_workspace_bytes(1, 8, 2, 1, 300, 96) == 0
     assert fa.fa_fwd_kvcache_workspace_bytes(1, 8, 3, 1, 300, 128) == 0
-    # a chunk holds at least 4 tiles of 32 keys, so a 300-row cache splits in
-    # ceil(10/4) = 3 chunks, rounded up to a multiple of the waves per workgroup
+    # one partial (query rows x (d outputs + 1 logsumexp), fp32) per wave of
+    # the split grid: 256 CUs x 4 resident waves at d = 128
     ws = fa.fa_fwd_kvcache_workspace_bytes(1, 8, 2, 1, 300, 128)
-    rows = 1 * 2 * 4 * 4                             # B * H_kv * S * (G * N_q)
+    rows = 1024 * 4                                  # waves * (G * N_q) rows
     assert ws == ((rows * 4 + 255) // 256) * 256 + rows * 128 * 4
-    # the workspace grows with the chunks, never with the cache itself
-    big = fa.fa_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128)
-    assert 0 < big < 8 * 8 * 32768 * 128 * 2 // 16
+    # it does not grow with the cache
+    assert fa.fa_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128) == ws
+    # at least one wave per (batch, K/V head, 32-row query group)
+    many = fa.fa_fwd_kvcache_workspace_bytes(2048, 8, 8, 1, 64, 128)
+    assert many == ((2048 * 8 * 4 + 255) // 256) * 256 + 2048 * 8 * 128 * 4
 
 
 def test_workspace_bytes(lib):

@@ -64,6 +64,8 @@ CASES = [
     (1, 4, 1, 1, 20000, 128, None),         # one group, a long cache in many chunks
     (2, 8, 1, 5, 129, 64, [129, 33]),       # 40 rows; ragged tail tiles
     (1, 2, 2, 7, 7, 256, None),             # N_q = N_kv: ordinary causal attention
+    (300, 4, 4, 1, 40, 64, None),           # more units than resident waves
+    (40, 8, 2, 2, 700, 128, "ragged"),      # a seeded mix of lengths, including 0
 ]
 
 
@@ -72,6 +74,10 @@ CASES = [
 def test_kvcache_small(case, causal):
     B, H, H_kv, N_q, N_kv, d, lens = case
     _say(f"kvcache {case} causal={causal}")
+    if lens == "ragged":
+        g = torch.Generator().manual_seed(B + N_kv)
+        lens = torch.randint(0, N_kv + 1, (B,), generator=g).tolist()
+        lens[:3] = [0, N_kv, 1]
     x = _inputs(B, H, H_kv, N_q, N_kv, d, lens, seed=sum(case[:6]) + causal)
     o, lse = _run(x, causal)
     o_ref, lse_ref = oracle.forward_kvcache(x["q_64"], x["k_64"], x["v_64"], x["lens"], x["scale"], causal)
