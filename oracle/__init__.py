@@ -25,6 +25,8 @@ from .attention import (  # noqa: F401
     forward,
     forward_rows,
     forward_kvcache,
+    forward_masked,
+    visible_range,
     backward_head,
     backward,
 )

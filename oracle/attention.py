@@ -103,6 +103,56 @@ def forward(q, k, v, scale=None, causal=True):
     return o, lse
 
 
+def visible_range(i, n, window, causal):
+    """Keys query i sees in a sequence of n valid tokens: [lo, hi] (empty if lo > hi).
+
+    The padding mask keeps keys below n (the 2D padding mask of
+    "FlashAttentionとは？…", TransformersのFA2における4Dマスクの非対応); the causal
+    mask of scores_rows keeps keys up to i; a sliding window of `window`
+    (local attention, named for Mistral-style models in the local-LLM guide
+    page) keeps keys from i - window on.
+    """
+    hi = min(i, n - 1) if causal else n - 1
+    lo = max(0, i - window) if window is not None and window >= 0 else 0
+    return lo, hi
+
+
+def forward_masked(q, k, v, seqlens=None, window=None, scale=None, causal=True):
+    """Attention with a per-sequence padding mask and an optional causal window.
+
+    q [B,H,N,d], k/v [B,H_kv,N,d]; sequence b is valid in rows 0..seqlens[b]-1
+    (all N when seqlens is None).  Query i < len_b sees the keys of
+    visible_range; rows at or past len_b are padding and are returned as
+    O = 0, LSE = -inf (the value of an empty softmax taken here).
+    """
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if window is not None and window >= 0 and not causal:
+        raise ValueError("a sliding window is causal")
+    lens = [N] * B if seqlens is None else [int(x) for x in seqlens]
+    if len(lens) != B or any(not 0 <= n <= N for n in lens):
+        raise ValueError("seqlens must hold B values in [0, N]")
+    o = np.zeros((B, H, N, v.shape[3]), dtype=np.float64)
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            continue
+        rows = np.arange(n)
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            keys, vals = k[b, kv, :n], v[b, kv, :n]         # the valid tokens
+            s = scores_rows(q[b, h, :n], keys, scale, causal, rows)
+            if window is not None and window >= 0:
+                cols = np.arange(keys.shape[0])[None, :]
+                s = np.where(cols >= rows[:, None] - window, s, -np.inf)
+            p, lse[b, h, :n] = softmax_rows(s)
+            o[b, h, :n] = p @ vals
+    return o, lse
+
+
 def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
     """Attention of a few new queries against a KV cache.
 

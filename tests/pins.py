@@ -3,7 +3,8 @@
 Each ``pin_*`` takes an implementation namespace ``impl`` exposing
 ``forward(q,k,v,scale,causal)``, ``forward_rows(q,k,v,scale,causal,rows)``,
 ``softmax_rows(s)``, ``scores_rows(...)``, ``backward(q,k,v,do,scale,causal)`` and
-``forward_kvcache(q,k,v,kv_len,scale,causal)``
+``forward_kvcache(q,k,v,kv_len,scale,causal)`` and
+``forward_masked(q,k,v,seqlens,window,scale,causal)``
 (the oracle, or a deliberately broken copy of it in the mutation test) and
 raises AssertionError when the implementation disagrees with:
 
@@ -15,7 +16,10 @@ raises AssertionError when the implementation disagrees with:
 * gradient identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i);
 * for the KV-cache forward: a scalar brute force over ragged cache lengths,
   the square case (ordinary attention), cache rows past the length being
-  ignored, identical keys, and the newest query seeing the whole cache.
+  ignored, identical keys, and the newest query seeing the whole cache;
+* for the padded / sliding-window forward: a scalar brute force, reductions
+  to plain attention (no mask, a window covering everything, a padded
+  sequence against its unpadded self) and window closed forms.
 """
 from __future__ import annotations
 
@@ -282,6 +286,84 @@ def pin_kvcache_last_query_sees_all(impl):
     assert np.max(np.abs(oc[:, :, 0] - on[:, :, 0])) > 1e-3   # earlier rows do differ
 
 
+# --------------------------------------------------- padding and window ---
+
+def brute_force_masked(q, k, v, lens, window, scale, causal):
+    """Scalar loops over each row's visible keys, written out independently."""
+    B, H, N, d = q.shape
+    g = H // k.shape[1]
+    o = np.zeros((B, H, N, v.shape[3]))
+    lse = np.full((B, H, N), -math.inf)
+    for b, h, i in itertools.product(range(B), range(H), range(N)):
+        n = int(lens[b])
+        if i >= n:
+            continue
+        js = [j for j in range(n) if (not causal or j <= i) and (window is None or window < 0 or j >= i - window)]
+        kv = h // g
+        s = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, kv, j, t]) for t in range(d)) for j in js]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = math.fsum(w)
+        lse[b, h, i] = mx + math.log(tot)
+        for t in range(v.shape[3]):
+            o[b, h, i, t] = math.fsum(wj * float(v[b, kv, j, t]) for wj, j in zip(w, js)) / tot
+    return o, lse
+
+
+def pin_masked_brute_force(impl):
+    rng = _rng(26)
+    cases = [(2, 4, 2, 9, 3, [9, 4], None, True), (2, 2, 1, 11, 4, [11, 0], 3, True),
+             (3, 2, 2, 8, 2, [1, 8, 5], 0, True), (2, 4, 4, 10, 3, [10, 6], None, False),
+             (1, 2, 1, 16, 5, [13], 7, True)]
+    for B, H, H_kv, N, d, lens, window, causal in cases:
+        q = rng.standard_normal((B, H, N, d)) * 1.5
+        k = rng.standard_normal((B, H_kv, N, d)) * 1.5
+        v = rng.standard_normal((B, H_kv, N, d))
+        o, lse = impl.forward_masked(q, k, v, lens, window, 0.6, causal)
+        o_b, lse_b = brute_force_masked(q, k, v, lens, window, 0.6, causal)
+        assert np.max(np.abs(o - o_b)) < 1e-13, (lens, window, causal)
+        fin = np.isfinite(lse_b)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.max(np.abs(lse[fin] - lse_b[fin]), initial=0.0) < 1e-13
+
+
+def pin_masked_reductions(impl):
+    """No padding and no window is plain attention; a window covering the whole
+    sequence changes nothing; a padded sequence equals the unpadded one."""
+    rng = _rng(27)
+    q = rng.standard_normal((2, 4, 12, 5))
+    k, v = rng.standard_normal((2, 2, 12, 5)), rng.standard_normal((2, 2, 12, 5))
+    for causal in (False, True):
+        o0, l0 = impl.forward(q, k, v, 0.5, causal)
+        o1, l1 = impl.forward_masked(q, k, v, None, None, 0.5, causal)
+        assert np.max(np.abs(o1 - o0)) < 1e-15 and np.max(np.abs(l1 - l0)) < 1e-15
+        om, lm = impl.forward_masked(q, k, v, [12, 7], None, 0.5, causal)
+        ot, lt = impl.forward(q[1:, :, :7], k[1:, :, :7], v[1:, :, :7], 0.5, causal)
+        assert np.max(np.abs(om[1, :, :7] - ot[0])) < 1e-14 and np.max(np.abs(lm[1, :, :7] - lt[0])) < 1e-14
+        assert np.all(om[1, :, 7:] == 0) and np.all(lm[1, :, 7:] == -math.inf)
+    o0, l0 = impl.forward(q, k, v, 0.5, True)
+    ow, lw = impl.forward_masked(q, k, v, None, 11, 0.5, True)
+    assert np.max(np.abs(ow - o0)) < 1e-15 and np.max(np.abs(lw - l0)) < 1e-15
+    ow, lw = impl.forward_masked(q, k, v, None, 10, 0.5, True)   # the last row loses key 0
+    assert np.max(np.abs(ow[:, :, :11] - o0[:, :, :11])) < 1e-15
+    assert np.max(np.abs(ow[:, :, 11] - o0[:, :, 11])) > 1e-6
+
+
+def pin_masked_window_closed_forms(impl):
+    """window 0: every row sees only itself (O_i = V_i, LSE_i = scale q_i.k_i);
+    window 1 with identical keys: the mean of V_{i-1} and V_i."""
+    rng = _rng(28)
+    q = rng.standard_normal((1, 2, 9, 4))
+    k, v = rng.standard_normal((1, 1, 9, 4)), rng.standard_normal((1, 1, 9, 4))
+    o, lse = impl.forward_masked(q, k, v, None, 0, 0.7, True)
+    assert np.max(np.abs(o[0] - v[0, 0][None])) < 1e-15
+    assert np.max(np.abs(lse[0] - 0.7 * np.einsum("hid,id->hi", q[0], k[0, 0]))) < 1e-14
+    k1 = np.repeat(k[:, :, :1], 9, axis=2)
+    o, lse = impl.forward_masked(q, k1, v, None, 1, 0.7, True)
+    want = np.concatenate([v[0, 0, :1], 0.5 * (v[0, 0, :-1] + v[0, 0, 1:])])
+    assert np.max(np.abs(o[0] - want[None])) < 1e-14
+
+
 # --------------------------------------------------------------- backward ---
 
 def _loss(impl, q, k, v, do, scale, causal):
@@ -338,7 +420,8 @@ def pin_gradient_identities(impl):
 FORWARD_PINS = [pin_rows_sum_to_one, pin_identical_keys, pin_dominant_key, pin_causal_row0,
                 pin_permutation_invariance, pin_shifts, pin_brute_force, pin_worked_example,
                 pin_forward_rows]
+MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms]
 KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
                 pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]
 BACKWARD_PINS = [pin_finite_differences, pin_gradient_identities]
-ALL_PINS = FORWARD_PINS + KVCACHE_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + KVCACHE_PINS + MASKED_PINS + BACKWARD_PINS

@@ -82,6 +82,38 @@ def test_kvcache_matches_torch_sdpa_fp64(shape, causal):
         assert np.max(np.abs(lse[b] - torch.logsumexp(s, -1)[0].numpy())) < 1e-12
 
 
+@pytest.mark.parametrize("case", [(2, 8, 2, 70, 16, 20, True), (3, 4, 4, 33, 8, None, True),
+                                  (2, 4, 2, 50, 32, None, False), (1, 2, 1, 64, 8, 0, True)])
+def test_masked_matches_torch_sdpa_fp64(case):
+    """Library cross-check of the padded / sliding-window forward: torch's CPU SDPA in
+    float64 on each unpadded sequence with a band mask built here."""
+    B, H, H_kv, N, d, window, causal = case
+    g = torch.Generator().manual_seed(N + d + (window or 0))
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64)
+    lens = torch.randint(1, N + 1, (B,), generator=g).tolist()
+    lens[0] = N
+    o, lse = oracle.forward_masked(q.numpy(), k.numpy(), v.numpy(), lens, window, None, causal)
+    rep = H // H_kv
+    for b, n in enumerate(lens):
+        kk = k[b:b + 1, :, :n].repeat_interleave(rep, 1)
+        vv = v[b:b + 1, :, :n].repeat_interleave(rep, 1)
+        i = torch.arange(n)[:, None]
+        j = torch.arange(n)[None, :]
+        mask = torch.ones(n, n, dtype=torch.bool)
+        if causal:
+            mask &= j <= i
+        if window is not None:
+            mask &= j >= i - window
+        ref = F.scaled_dot_product_attention(q[b:b + 1, :, :n], kk, vv, attn_mask=mask)
+        assert np.max(np.abs(o[b, :, :n] - ref[0].numpy())) < 1e-12
+        assert np.all(o[b, :, n:] == 0) and np.all(lse[b, :, n:] == -np.inf)
+        s = (q[b:b + 1, :, :n] @ kk.transpose(-1, -2)) / math.sqrt(d)
+        s = s.masked_fill(~mask, float("-inf"))
+        assert np.max(np.abs(lse[b, :, :n] - torch.logsumexp(s, -1)[0].numpy())) < 1e-12
+
+
 def _page_fp32_errors():
     path = os.path.join(os.path.dirname(__file__), "golden", "cpu_sdpa_fp32_error.txt")
     out = {}
@@ -132,6 +164,10 @@ MUTANTS = {
     "kvcache_off_by_one": ("pos = n - n_q + np.arange(n_q)", "pos = n - n_q + 1 + np.arange(n_q)"),
     "kvcache_whole_cache": ("s = scores_rows(q[b, h, rows], k[b, kv, :n],", "s = scores_rows(q[b, h, rows], k[b, kv],"),
     "kvcache_empty_rows_nan": ("rows = np.flatnonzero(n_seen > 0)", "rows = np.arange(n_q)"),
+    "window_off_by_one": ("s = np.where(cols >= rows[:, None] - window, s, -np.inf)",
+                          "s = np.where(cols > rows[:, None] - window, s, -np.inf)"),
+    "window_ignored": ("s = np.where(cols >= rows[:, None] - window, s, -np.inf)", "s = s"),
+    "padding_keys_kept": ("keys, vals = k[b, kv, :n], v[b, kv, :n]", "keys, vals = k[b, kv], v[b, kv]"),
     "kvcache_v_whole_cache": ("o[b, h, rows] = p @ v[b, kv, :n]", "o[b, h, rows] = p @ v[b, kv, :p.shape[1]][::-1]"),
 }
 
