@@ -17,7 +17,8 @@ The JSON line also carries:
                 causal bf16 d=128 forward, the fp32 and fp8 forwards, the
                 bf16 backward (fwd+bwd) at its full size, and the KV-cache
                 (decode) forward as the rate it reads the cache at, against
-                the 8 TB/s HBM peak.
+                the 8 TB/s HBM peak, and the padded / sliding-window forward
+                (FLOPs of the visible pairs only).
 """
 from __future__ import annotations
 
@@ -37,6 +38,7 @@ HBM_GBS = 8000.0
 STEP = ["C2a", "C2a_nc", "C2b"]
 EXTRA_FWD = ["Ta", "Ta_gqa", "Tb", "Tc", "C1", "C3", "C5"]
 EXTRA_KV = ["D1", "D1_ragged"]
+EXTRA_MASKED = ["W1", "P1"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_kvcache.hip", "fa_common.hpp")]
@@ -131,6 +133,33 @@ class KvCase:
                 "cache_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_GBS, 4),
                 "cache_bytes": self.w.cache_bytes(self.lens),
                 "tflops": round(self.w.flops(self.lens) / (ms * 1e-3) / 1e12, 3)}
+
+
+class MaskedCase:
+    """Device-resident inputs of one padded / sliding-window workload."""
+
+    def __init__(self, name, dev):
+        import torch
+        import synthetic as syn
+        self.w = w = syn.MASKED_WORKLOADS[name]
+        x = syn.make_masked_inputs(w)
+        self.lens = x["lens"]
+        self.scale = x["scale"]
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.seqlens = x["seqlens"].to(dev) if x["seqlens"] is not None else None
+        self.o = torch.empty(w.B, w.H, w.N, w.d, device=dev, dtype=torch.bfloat16)
+        self.lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
+
+    def fwd(self):
+        import exact_tiled_attention_amd as fa
+        fa.fa_fwd_masked(self.q, self.k, self.v, self.seqlens, self.w.window, causal=self.w.causal,
+                         scale=self.scale, out=self.o, lse=self.lse)
+
+    def report(self, ms):
+        tf = self.w.flops_fwd(self.lens) / (ms * 1e-3) / 1e12
+        return {"kernel": f"fwd_bf16_d{self.w.d}_masked", "ms": round(ms, 4), "tflops": round(tf, 2),
+                "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "window": self.w.window,
+                "valid_rows": int(sum(self.lens))}
 
 
 def log(msg):
@@ -255,6 +284,18 @@ def main():
                           "config": {"workload": args.only}, "decode": rep}))
         return
 
+    if args.only in syn.MASKED_WORKLOADS:
+        c = MaskedCase(args.only, dev)
+        xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
+        rep = c.report(median(xs))
+        log(f"{args.only}: {rep}")
+        print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
+                          "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": rep["ms"], "higher_is_better": True,
+                          "dtype": "bf16", "data": "synthetic", "config": {"workload": args.only},
+                          "masked": rep}))
+        return
+
     names = [args.only] if args.only else STEP
     cases = [Case(n, dev, backward=syn_workload(n).backward and bool(args.only)) for n in names]
     step_flops = sum(c.w.flops_fwd() + (c.w.flops_bwd() if c.backward else 0.0) for c in cases)
@@ -325,6 +366,12 @@ def main():
             tf = c.w.flops_fwd() / (ms * 1e-3) / 1e12
             extra[name] = {"kernel": kernel_name(c.w), "ms": round(ms, 4), "tflops": round(tf, 2),
                            "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
+            del c
+            torch.cuda.empty_cache()
+        for name in EXTRA_MASKED:
+            log(f"extra: {name}")
+            c = MaskedCase(name, dev)
+            extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
             del c
             torch.cuda.empty_cache()
         for name in EXTRA_KV:

@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+__all__ = ["fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
            "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
            "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
 
@@ -25,7 +25,7 @@ FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE",
                 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_INVALID_VALUE", 5: "FA_ERR_WORKSPACE",
                 6: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+EXPORTED = ("fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
             "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
             "fa_status_string")
 
@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_masked.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -155,6 +157,33 @@ def fa_fwd(q, k, v, causal: bool = True, scale: float | None = None,
     code = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                       _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
                       B, H, H_kv, N, d, float(scale), int(bool(causal)), dt, _stream())
+    _check(code)
+    return out, lse
+
+
+def fa_fwd_masked(q, k, v, seqlens=None, window: int | None = None, causal: bool = True,
+                  scale: float | None = None, out=None, lse=None, want_lse: bool = True):
+    """O, LSE with a padding mask (seqlens: int32 device tensor [B] of valid rows,
+    or None) and/or a causal sliding window (query i sees keys i - window .. i)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, N, d = _shape(q, k, v)
+    codes = DTYPE_CODES()
+    if q.dtype not in codes:
+        raise FaError(3, f"unsupported dtype {q.dtype}")
+    dt = codes[q.dtype]
+    if seqlens is not None and (seqlens.dtype != torch.int32 or not seqlens.is_cuda
+                                or not seqlens.is_contiguous() or tuple(seqlens.shape) != (B,)):
+        raise ValueError("seqlens must be a contiguous int32 device tensor of shape [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(B, H, N, d, device=q.device, dtype=torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    code = lib.fa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqlens),
+                             -1 if window is None else int(window), B, H, H_kv, N, d, float(scale),
+                             int(bool(causal)), dt, _stream())
     _check(code)
     return out, lse
 

@@ -97,12 +97,46 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   p.qs = q_descale; p.ks = k_descale; p.vs = v_descale;
   p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.seqlens = nullptr;
+  p.window = -1;
   hipError_t e;
   switch (dtype) {
     case FA_DTYPE_F32: e = fa::launch_fwd_f32(d, causal != 0, p, stream); break;
     case FA_DTYPE_BF16: e = fa::launch_fwd_bf16(d, causal != 0, p, stream); break;
     default: e = fa::launch_fwd_fp8(d, causal != 0, p, stream); break;
   }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        const int* seqlens, int window, int B, int H, int H_kv, int N, int d,
+                        float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+  if (!Q || !K || !V || !O) return FA_ERR_NULL_POINTER;
+  if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
+  if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
+  if (dtype != FA_DTYPE_BF16 || !fa_supported(dtype, d, 0)) return FA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
+  if (window >= 0 && !causal) return FA_ERR_INVALID_VALUE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+    return FA_ERR_INVALID_VALUE;
+  const size_t eb = elem_bytes(dtype);
+  const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
+  const size_t ob = (size_t)B * H * N * d * out_bytes(dtype), lb = LSE ? (size_t)B * H * N * 4 : 0;
+  const size_t sb = seqlens ? (size_t)B * 4 : 0;
+  const void* ins[] = {Q, K, V, seqlens};
+  const size_t insz[] = {nq, nkv, nkv, sb};
+  for (int j = 0; j < 4; ++j)
+    if (overlap(O, ob, ins[j], insz[j]) || overlap(LSE, lb, ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
+  if (overlap(LSE, lb, O, ob)) return FA_ERR_INVALID_VALUE;
+
+  fa::FwdParams p{};
+  p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.seqlens = seqlens;
+  p.window = window < 0 ? -1 : window;
+  const hipError_t e = fa::launch_fwd_bf16(d, causal != 0, p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

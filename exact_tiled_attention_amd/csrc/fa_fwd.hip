@@ -64,6 +64,36 @@
 
 namespace fa {
 
+// ------------------------------------------------------ mask variants -----
+// The per-sequence padding mask and the causal sliding window shrink the
+// keys a query sees: query i of sequence b (valid for its first len_b rows)
+// sees keys max(0, i - window) .. min(i, len_b - 1) (causal) or
+// 0 .. len_b - 1; rows at or past len_b are padding and get O = 0,
+// LSE = -inf.  Only the tile range and the element mask change.
+struct ItemMask {
+  int len;       // valid rows of the sequence (N without a padding mask)
+  int window;    // < 0: none
+  int t_begin;   // first key tile that any row of the item sees
+};
+template <bool MASK>
+__device__ __forceinline__ ItemMask mask_of(const FwdParams& p, int b, int q_first, int bc) {
+  ItemMask m{p.N, -1, 0};
+  if constexpr (MASK) {
+    m.len = p.seqlens ? min(max(p.seqlens[b], 0), p.N) : p.N;
+    m.window = p.window;
+    if (p.window >= 0) m.t_begin = max(0, q_first - p.window) / bc;
+  }
+  return m;
+}
+// O = 0 (bf16) and LSE = -inf for a padding row; lanes l and l ^ 32 each
+// write half of the row.
+__device__ __forceinline__ void write_empty_rows(const FwdParams& p, int bh, int myq, int g, int d) {
+  if (myq >= p.N) return;
+  bf16* orow = (bf16*)p.o + ((size_t)bh * p.N + myq) * d;
+  for (int c = 4 * g; c < d; c += 8) *(i32x2*)(orow + c) = i32x2{0, 0};
+  if (p.lse && g == 0) p.lse[(size_t)bh * p.N + myq] = -INFINITY;
+}
+
 // ===================================================== bf16 / fp8 ========
 template <int D, bool CAUSAL, bool FP8>
 struct FwdCfg {
@@ -376,7 +406,7 @@ struct Bf16Cfg {
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
   static_assert(2 * IPW * (NST - 2) < 64, "DMA count must fit the vmcnt field");
 };
-template <int D, bool CAUSAL, int NW, int BC_, int NST>
+template <int D, bool CAUSAL, int NW, int BC_, int NST, bool MASK>
 __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const WorkItem wi) {
   using C = Bf16Cfg<D, NW, BC_, NST>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
@@ -397,8 +427,15 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   const int q_first = wi.qt * BR;
   const int q0 = q_first + wid * 32;
   const int myq = q0 + lr;
-  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
+  const ItemMask mk = mask_of<MASK>(p, b, q_first, BC);
+  const int L = mk.len;
+  if (MASK && q_first >= L) {           // every row of the item is padding
+    write_empty_rows(p, wi.bh, myq, g, D);
+    return;
+  }
+  const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
+  const int t0 = mk.t_begin;            // tiles j = 0.. stand for t0 + j
+  const int n_tiles = (kv_end + BC - 1) / BC - t0;
 
   // Q operand (B of S^T = K Q^T): slot (kb, g, e) <-> column kb*16 + 8g + e.
   bf16x8 qr[D / 16];
@@ -438,8 +475,8 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   float m_run = -INFINITY, l_run = 0.f;
 
   auto issue = [&](int j, unsigned char* st) {
-    const int key0 = j * BC;
-    const int bytes = min(N - key0, BC) * RB;   // rows past the end read as zero
+    const int key0 = (t0 + j) * BC;
+    const int bytes = min(L - key0, BC) * RB;   // rows past the end read as zero
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
 #pragma unroll
@@ -451,8 +488,9 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
 
   auto consume = [&](int j, const unsigned char* kl) {
     const unsigned char* vl = kl + C::TILE;
-    const int key0 = j * BC;
+    const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;   // every key of the tile follows every row of the wave
+    if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return;   // below every row's window
     f32x16 s[BC / 32];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
@@ -476,13 +514,15 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
       }
       __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
     }
-    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+    if ((key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0) ||
+        (MASK && mk.window >= 0 && key0 < q0 + 31 - mk.window)) {
 #pragma unroll
       for (int kb32 = 0; kb32 < BC / 32; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
+          if ((CAUSAL && key > myq) || key >= L || (MASK && mk.window >= 0 && key < myq - mk.window))
+            s[kb32][r] = -INFINITY;
         }
     }
     // P against the running max first; the tile max is only taken when some
@@ -522,14 +562,17 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
       mx = max_halves(mx);
       const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
+      // (with MASK a row may have seen no key yet: it keeps m = -inf, l = 0,
+      // O = 0 and takes its exponentials against 0, so masked scores give 0)
+      const bool none = MASK && m_new == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      ts = expo(m_run);
+      ts = expo(none ? 0.f : m_run);
     }
     l_run += ts;
 #pragma unroll
@@ -576,7 +619,9 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   }
 
   const float l_tot = sum_halves(l_run);
-  if (myq < N) {
+  if (MASK && myq >= L) {
+    write_empty_rows(p, wi.bh, myq, g, D);
+  } else if (myq < N) {
     const float inv = 1.f / l_tot;
     bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
 #pragma unroll
@@ -592,7 +637,7 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   }
 }
 
-template <int D, bool CAUSAL, int NW, int BC_, int NST, bool PERSIST>
+template <int D, bool CAUSAL, int NW, int BC_, int NST, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
   if constexpr (PERSIST) {
@@ -600,10 +645,11 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
-      fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST>(p, item_of(w, p.n_qt));
+      if (r > 0) __syncthreads();
+      fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
   }
 }
 
@@ -634,8 +680,10 @@ struct PpCfg {
   static_assert(2 * IPD < 64, "DMA count must fit the vmcnt field");
 };
 
-// One work item (head, 256-row query tile) of the ping-pong kernel.
-template <int D, bool CAUSAL, int BC_, bool LATE>
+// One work item (head, 256-row query tile) of the ping-pong kernel.  With
+// MASK, sequence b is valid for its first len_b rows (p.seqlens) and, with a
+// window w >= 0, query i sees only keys i - w .. i (see mask_of).
+template <int D, bool CAUSAL, int BC_, bool LATE, bool MASK>
 __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   using C = PpCfg<D, BC_, LATE>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPD = C::IPD, NKB = C::NKB, NST = C::NST;
@@ -659,8 +707,15 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   const int q_first = wi.qt * BR;
   const int q0 = q_first + wid * 32;
   const int myq = q0 + lr;
-  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
+  const ItemMask mk = mask_of<MASK>(p, b, q_first, BC);
+  const int L = mk.len;                 // valid rows (N without MASK)
+  if (MASK && q_first >= L) {           // every row of the item is padding
+    write_empty_rows(p, wi.bh, myq, g, D);
+    return;
+  }
+  const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
+  const int t0 = mk.t_begin;            // first key tile any row of the item sees
+  const int n_tiles = (kv_end + BC - 1) / BC - t0;   // tiles j = 0.. stand for t0 + j
 
   bf16x8 qr[D / 16];
 #pragma unroll
@@ -699,8 +754,8 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   bf16x8 pk[NKB][2];
 
   auto issue_one = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
-    const int key0 = j * BC;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+    const int key0 = (t0 + j) * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(L - key0, BC) * RB);
 #pragma unroll
     for (int i = 0; i < IPD; ++i) dma16_buf<0>(r, off[i], st + (dwid * IPD + i) * 1024);
   };
@@ -708,8 +763,9 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   // the online softmax of S_j into P_j (packed bf16).
   f32x16 s[NKB];
   auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {
-    const int key0 = j * BC;
+    const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return false;
+    if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return false;   // below every row's window
     // consecutive MFMAs go to different accumulators (no back-to-back chain)
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
@@ -733,16 +789,26 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
     return true;
   };
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int key0 = j * BC;
-    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+    const int key0 = (t0 + j) * BC;
+    if ((key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0)) {
       // key = key0 + 4g + rel, rel a compile-time constant per register
-      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+      const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
 #pragma unroll
       for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
           if (rel > lim) s[kb32][r] = -INFINITY;
+        }
+    }
+    if (MASK && mk.window >= 0 && key0 < q0 + 31 - mk.window) {
+      const int lo = myq - mk.window - key0 - 4 * g;   // first visible rel of this row
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel < lo) s[kb32][r] = -INFINITY;
         }
     }
     // P against the running max first; the tile max is only taken when some
@@ -779,14 +845,17 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
       mx = max_halves(mx);
       const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
+      // (with MASK a row may have seen no key yet: it keeps m = -inf, l = 0,
+      // O = 0 and takes its exponentials against 0, so masked scores give 0)
+      const bool none = MASK && m_new == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      ts = expo(m_run);
+      ts = expo(none ? 0.f : m_run);
     }
     l_run += ts;
   };
@@ -889,7 +958,9 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   }
 
   const float l_tot = sum_halves(l_run);
-  if (myq < N) {
+  if (MASK && myq >= L) {
+    write_empty_rows(p, wi.bh, myq, g, D);
+  } else if (myq < N) {
     const float inv = 1.f / l_tot;
     bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
 #pragma unroll
@@ -906,8 +977,10 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
 }
 
 // With PERSIST, one workgroup per CU loops over its share of the items (see
-// persistent_map); otherwise one workgroup per item.
-template <int D, bool CAUSAL, int BC_, bool LATE, bool PERSIST>
+// persistent_map); otherwise one workgroup per item.  Between items the
+// workgroup synchronises: an item's first DMAs must not land in a stage a
+// slower wave is still reading for the previous item.
+template <int D, bool CAUSAL, int BC_, bool LATE, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pp_kernel(FwdParams p) {
   if constexpr (PERSIST) {
@@ -915,10 +988,11 @@ void fwd_bf16_pp_kernel(FwdParams p) {
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
-      pp_item<D, CAUSAL, BC_, LATE>(p, item_of(w, p.n_qt));
+      if (r > 0) __syncthreads();
+      pp_item<D, CAUSAL, BC_, LATE, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    pp_item<D, CAUSAL, BC_, LATE>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    pp_item<D, CAUSAL, BC_, LATE, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
   }
 }
 
@@ -949,7 +1023,7 @@ struct PairCfg {
   static_assert(IPW >= 1, "tile too small for the DMA split");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, const WorkItem wi) {
   using C = PairCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, DH = C::DH;
@@ -975,10 +1049,18 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   const int q_first = wi.qt * BR;
   const int q0 = q_first + pr * 32;              // first row of the pair
   const int myq = q0 + lr;
-  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  // tiles the pair takes part in: 0 .. t_end - 1
-  const int t_end = CAUSAL ? min(n_tiles, (q0 + 31) / BC + 1) : n_tiles;
+  const ItemMask mk = mask_of<MASK>(p, b, q_first, BC);
+  const int L = mk.len;
+  if (MASK && q_first >= L) {                    // every row of the item is padding
+    if (role == 0) write_empty_rows(p, wi.bh, myq, g, D);
+    return;
+  }
+  const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
+  const int t0 = mk.t_begin;                     // tiles t = 0.. stand for t0 + t
+  const int n_tiles = (kv_end + BC - 1) / BC - t0;
+  // tiles the pair takes part in: t_beg .. t_end - 1
+  const int t_end = CAUSAL ? min(n_tiles, (q0 + 31) / BC + 1 - t0) : n_tiles;
+  const int t_beg = MASK && mk.window >= 0 ? max(0, q0 - mk.window) / BC - t0 : 0;
 
   bf16x8 qr[D / 16];
 #pragma unroll
@@ -1023,8 +1105,8 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   float* sb = sbuf + pr * 64 + lane;
 
   auto issue = [&](const unsigned char* src, const int* off, int t, unsigned char* st) {
-    const int key0 = t * BC;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+    const int key0 = (t0 + t) * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(L - key0, BC) * RB);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
   };
@@ -1053,7 +1135,8 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   auto rebase = [&](float m_t, float ts_t) {
     if (__any(m_t > m_ref)) {
       const float m_new = fmaxf(m_ref, m_t);
-      const float alpha = fast_exp2(m_ref - m_new);
+      // (with MASK a row may still have seen no key: both maxima -inf)
+      const float alpha = MASK && m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -1082,15 +1165,25 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   };
   // Softmax of S_t against m_prev; leaves P_t in pk and publishes it.
   auto softmax = [&](int t, float m_prev) {
-    const int key0 = t * BC;
-    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
-      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+    const int key0 = (t0 + t) * BC;
+    if ((key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0)) {
+      const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
 #pragma unroll
       for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
           if (rel > lim) s[kb32][r] = -INFINITY;
+        }
+    }
+    if (MASK && mk.window >= 0 && key0 < q0 + 31 - mk.window) {
+      const int lo = myq - mk.window - key0 - 4 * g;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel < lo) s[kb32][r] = -INFINITY;
         }
     }
     auto expo = [&](float m) -> float {
@@ -1125,7 +1218,9 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
       mx = max_halves(mx);
       m = fmaxf(m, mx * c);
-      ts = expo(m);
+      // (with MASK a row may have seen no key yet: m stays -inf and the
+      // exponentials are taken against 0, so masked scores give 0)
+      ts = expo(MASK && m == -INFINITY ? 0.f : m);
     }
     m_own = m;
     ts_own = sum_halves(ts);
@@ -1150,19 +1245,19 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   };
   auto as_owner = [&](int ph, const unsigned char* v_use) {
     // the partner's tile ph - 1: its max, row sums and P come from LDS
-    const float m_prev = ph >= 1 ? *mb : -INFINITY;
-    if (ph >= 1 && ph - 1 < t_end) {
+    const float m_prev = ph > t_beg ? *mb : -INFINITY;
+    if (ph - 1 >= t_beg && ph - 1 < t_end) {
       rebase(m_prev, *sb);
       pv(v_use, true);
     }
-    if (ph >= 0 && ph < t_end) softmax(ph, m_prev);
+    if (ph >= t_beg && ph < t_end) softmax(ph, m_prev);
   };
   auto as_other = [&](int ph, const unsigned char* k_use, const unsigned char* v_use) {
-    if (ph >= 1 && ph - 1 < t_end) {
+    if (ph - 1 >= t_beg && ph - 1 < t_end) {
       rebase(m_own, ts_own);
       pv(v_use, false);
     }
-    if (ph + 1 < t_end) qk(k_use);
+    if (ph + 1 >= t_beg && ph + 1 < t_end) qk(k_use);
   };
 
   issue(kg, dma_k, 0, k0);
@@ -1188,7 +1283,9 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
 
   // l_run already holds whole-row sums (the published sums were combined
   // across the two halves of the wave).
-  if (myq < N) {
+  if (MASK && myq >= L) {
+    if (role == 0) write_empty_rows(p, wi.bh, myq, g, D);
+  } else if (myq < N) {
     const float inv = 1.f / l_run;
     bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D + role * DH;
 #pragma unroll
@@ -1204,7 +1301,7 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   }
 }
 
-template <int D, bool CAUSAL, bool PERSIST>
+template <int D, bool CAUSAL, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pairs_kernel(FwdParams p) {
   if constexpr (PERSIST) {
@@ -1212,10 +1309,11 @@ void fwd_bf16_pairs_kernel(FwdParams p) {
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
-      fwd_bf16_pairs_kernel_item<D, CAUSAL>(p, item_of(w, p.n_qt));
+      if (r > 0) __syncthreads();
+      fwd_bf16_pairs_kernel_item<D, CAUSAL, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    fwd_bf16_pairs_kernel_item<D, CAUSAL>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    fwd_bf16_pairs_kernel_item<D, CAUSAL, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
   }
 }
 
@@ -1470,7 +1568,10 @@ static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
   // looping instance measured slower (C4 forward: 789 vs 937 TFLOP/s)
   using C = Bf16Cfg<D, NW, BC, NST>;
   finish_grid(p, C::BR);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false>), dim3(p.total), dim3(C::NT), 0, s, p);
+  if (masked(p))
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, true>), dim3(p.total), dim3(C::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, false>), dim3(p.total), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1478,7 +1579,10 @@ template <int D, bool CAUSAL>
 static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
   // one workgroup per item: the looping instance spills a register
   finish_grid(p, PairCfg<D>::BR);
-  hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL, false>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
+  if (masked(p))
+    hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL, false, true>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL, false, false>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1486,9 +1590,14 @@ template <int D, bool CAUSAL, int BC, bool LATE>
 static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
   using C = PpCfg<D, BC, LATE>;
   finish_grid(p, C::BR);
+  if (masked(p)) {
+    static std::atomic<int> occ_m[64];
+    return launch_items(fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, true, true>,
+                        fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, false, true>, C::NT, p, s, occ_m);
+  }
   static std::atomic<int> occ[64];
-  return launch_items(fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, true>, fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, false>,
-                      C::NT, p, s, occ);
+  return launch_items(fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, true, false>,
+                      fwd_bf16_pp_kernel<D, CAUSAL, BC, LATE, false, false>, C::NT, p, s, occ);
 }
 
 // Kernel choice per (head dim, mask), from measurements on MI355X:

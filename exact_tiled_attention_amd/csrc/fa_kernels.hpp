@@ -20,7 +20,12 @@ struct FwdParams {
   int total;           // B * H * n_qt work items (= grid size)
   int remap;           // 1: XCD-contiguous work map
   float scale_log2;    // scale * log2(e)
+  const int* seqlens;  // [B] valid rows per sequence (padding mask), or null
+  int window;          // causal sliding window: query i sees keys i - window .. i; < 0: none
 };
+
+// True when a forward call carries a padding mask or a sliding window.
+inline bool masked(const FwdParams& p) { return p.seqlens != nullptr || p.window >= 0; }
 
 struct BwdParams {
   const void* q;

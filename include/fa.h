@@ -88,6 +88,29 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
                  fa_dtype dtype, hipStream_t stream);
 
 /*
+ * Forward pass with a padding mask and/or a causal sliding window (local
+ * attention).  Transformers' FA2 takes a 2D padding mask ("FlashAttentionとは？
+ * …", section TransformersのFA2における4Dマスクの非対応); models that use
+ * sliding-window attention are named in the local-LLM guide page (section on
+ * models with non-standard sliding-window attention).  Arguments as in fa_fwd
+ * (no fp8 descales), plus:
+ *   seqlens: DEVICE int32 [B], or NULL.  Sequence b holds valid tokens in rows
+ *     0 .. seqlens[b] - 1 of Q, K and V (right padding); keys past it are
+ *     never seen, and its query rows past it are written as O = 0,
+ *     LSE = -inf.  Values are clamped to [0, N] on the device.
+ *   window: < 0 for none; >= 0 (causal only) lets query i see keys
+ *     i - window .. i, i.e. window + 1 keys.
+ * So query i of sequence b (i < len_b) sees keys max(0, i - window) ..
+ * min(i, len_b - 1) when causal, 0 .. len_b - 1 otherwise.
+ * Supported: BF16 with d = 64, 128, 256; FA_ERR_UNSUPPORTED otherwise.
+ * FA_ERR_INVALID_VALUE for window >= 0 without causal, or a seqlens pointer
+ * that is not 4-byte aligned or overlaps an output.
+ */
+fa_status fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        const int* seqlens, int window, int B, int H, int H_kv, int N, int d,
+                        float scale, int causal, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for this problem (0 on invalid
  * arguments).  The workspace holds two fp32 [B][H][N] arrays: D = rowsum(dO * O)
  * and the forward's LSE in base-2 units.

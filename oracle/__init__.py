@@ -26,6 +26,7 @@ from .attention import (  # noqa: F401
     forward_rows,
     forward_kvcache,
     forward_masked,
+    forward_masked_rows,
     visible_range,
     backward_head,
     backward,

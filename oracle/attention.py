@@ -153,6 +153,24 @@ def forward_masked(q, k, v, seqlens=None, window=None, scale=None, causal=True):
     return o, lse
 
 
+def forward_masked_rows(q, k, v, n, window, scale, causal, rows):
+    """Selected query rows of one head of forward_masked (q [N,d], k/v [N_k,d]),
+    for sequence length n: each row's visible keys of visible_range, taken one
+    row at a time."""
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.zeros((rows.size, v.shape[1]))
+    lse = np.full(rows.size, -np.inf)
+    for t, i in enumerate(rows):
+        if i >= n:
+            continue
+        lo, hi = visible_range(int(i), n, window, causal)
+        s = scale * (k[lo:hi + 1] @ q[i])
+        p, l = softmax_rows(s[None, :])
+        o[t] = p[0] @ v[lo:hi + 1]
+        lse[t] = l[0]
+    return o, lse
+
+
 def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
     """Attention of a few new queries against a KV cache.
 

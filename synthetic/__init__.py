@@ -252,3 +252,61 @@ def make_kvcache_inputs(w: KvCacheWorkload):
     out["kv_len"] = cache_lengths(w.B, w.N_kv, w.seed) if w.ragged else None
     out["lens"] = out["kv_len"].tolist() if w.ragged else [w.N_kv] * w.B
     return out
+
+
+# ------------------------------------------- padding mask / sliding window ---
+
+@dataclass(frozen=True)
+class MaskedWorkload:
+    """A forward with a per-sequence padding mask (``ragged``: seeded valid
+    lengths in [1, N]) and/or a causal sliding window (query i sees keys
+    i - window .. i)."""
+
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    N: int
+    d: int
+    dtype: str = "bf16"
+    causal: bool = True
+    amp: float = 1.0
+    seed: int = 0
+    window: int | None = None
+    ragged: bool = False
+    note: str = field(default="", compare=False)
+
+    def visible_pairs(self, lens) -> int:
+        """(query, key) pairs the mask leaves, summed over sequences (per head)."""
+        tot = 0
+        for n in lens:
+            i = torch.arange(int(n), dtype=torch.int64)
+            hi = i if self.causal else torch.full_like(i, int(n) - 1)
+            lo = (i - self.window).clamp(min=0) if self.window is not None else torch.zeros_like(i)
+            tot += int((hi - lo + 1).clamp(min=0).sum())
+        return tot
+
+    def flops_fwd(self, lens) -> float:
+        """4 * d flops per visible pair and query head."""
+        return 4.0 * self.H * self.d * self.visible_pairs(lens)
+
+
+# Prefill with the GQA head layout of the stated prefill shape: a 4096-key
+# sliding window (each query sees itself and 4095 earlier keys) at N = 8192,
+# and a right-padded batch of seeded lengths at N = 4096.  Seeds 12+.
+MASKED_WORKLOADS = {
+    "W1": MaskedWorkload("W1", 4, 32, 8, 8192, 128, seed=12, window=4095,
+                         note="causal sliding window of 4096 keys"),
+    "P1": MaskedWorkload("P1", 8, 32, 8, 4096, 128, seed=13, ragged=True,
+                         note="right-padded batch, seeded valid lengths in [1, 4096]"),
+}
+
+
+def make_masked_inputs(w: MaskedWorkload):
+    """pack_inputs of the workload's draws plus ``seqlens`` (int32 CPU tensor
+    or None) and ``lens`` (the lengths as a list, N each when not ragged)."""
+    q, k, v, _ = draw(w.B, w.H, w.H_kv, w.N, w.d, w.amp, w.seed)
+    out = pack_inputs(q, k, v, None, w.dtype)
+    out["seqlens"] = cache_lengths(w.B, w.N, w.seed) if w.ragged else None
+    out["lens"] = out["seqlens"].tolist() if w.ragged else [w.N] * w.B
+    return out

@@ -420,7 +420,22 @@ def pin_gradient_identities(impl):
 FORWARD_PINS = [pin_rows_sum_to_one, pin_identical_keys, pin_dominant_key, pin_causal_row0,
                 pin_permutation_invariance, pin_shifts, pin_brute_force, pin_worked_example,
                 pin_forward_rows]
-MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms]
+def pin_masked_rows(impl):
+    """Row subsets of one head agree with the whole-sequence computation."""
+    rng = _rng(29)
+    q = rng.standard_normal((1, 1, 30, 4))
+    k, v = rng.standard_normal((1, 1, 30, 4)), rng.standard_normal((1, 1, 30, 4))
+    rows = [0, 5, 17, 21, 29]
+    for n, window, causal in ((30, None, True), (22, 6, True), (25, None, False), (30, 0, True)):
+        of, lf = impl.forward_masked(q, k, v, [n], window, 0.9, causal)
+        orow, lrow = impl.forward_masked_rows(q[0, 0], k[0, 0], v[0, 0], n, window, 0.9, causal, rows)
+        assert np.max(np.abs(orow - of[0, 0, rows])) < 1e-14
+        fin = np.isfinite(lf[0, 0, rows])
+        assert np.array_equal(np.isfinite(lrow), fin)
+        assert np.max(np.abs(lrow[fin] - lf[0, 0, rows][fin]), initial=0.0) < 1e-14
+
+
+MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows]
 KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
                 pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]
 BACKWARD_PINS = [pin_finite_differences, pin_gradient_identities]

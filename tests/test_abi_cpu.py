@@ -112,6 +112,24 @@ def test_bwd_validation(lib):
     assert bwd(lib, ptrs=[P * (i + 1) for i in range(8)] + [P]) == 4   # dV aliases Q
 
 
+def fwdm(lib, q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, seqlens=None, window=-1, B=2, H=2, Hkv=2, N=16,
+         d=64, scale=0.125, causal=1, dtype=1):
+    return lib.fa_fwd_masked(q, k, v, o, lse, seqlens, window, B, H, Hkv, N, d, scale, causal, dtype, None)
+
+
+def test_masked_validation(lib):
+    assert fwdm(lib, q=None) == 1
+    assert fwdm(lib, N=0) == 2
+    assert fwdm(lib, dtype=0) == 3                   # bf16 only
+    assert fwdm(lib, dtype=2, d=128) == 3
+    assert fwdm(lib, d=96) == 3
+    assert fwdm(lib, scale=0.0) == 4
+    assert fwdm(lib, window=8, causal=0) == 4        # a window is causal
+    assert fwdm(lib, seqlens=6 * P + 2) == 4         # not 4-byte aligned
+    assert fwdm(lib, seqlens=4 * P + 8) == 4         # inside O
+    assert fwdm(lib, lse=4 * P + 64) == 4            # LSE inside O
+
+
 def kvc(lib, q=P, k=2 * P, v=3 * P, kv_len=None, o=4 * P, lse=5 * P, ws=64 * P, ws_bytes=1 << 30,
         B=2, H=8, Hkv=2, Nq=1, Nkv=300, d=128, scale=0.08, causal=1, dtype=1):
     return lib.fa_fwd_kvcache(q, k, v, kv_len, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, scale,
