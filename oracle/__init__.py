@@ -27,6 +27,7 @@ from .attention import (  # noqa: F401
     forward_kvcache,
     forward_masked,
     forward_masked_rows,
+    backward_masked,
     visible_range,
     backward_head,
     backward,

@@ -171,6 +171,40 @@ def forward_masked_rows(q, k, v, n, window, scale, causal, rows):
     return o, lse
 
 
+def backward_masked(q, k, v, do, seqlens=None, window=None, scale=None, causal=True):
+    """Gradients of L = sum(O * dO) for forward_masked.
+
+    Only the valid tokens of each sequence take part: the chain rule of
+    backward_head runs on the unpadded sequence with the window applied to its
+    scores, and padding rows and keys get zero gradients (padding outputs are
+    the constant 0, so their dO does not matter).
+    """
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    lens = [N] * B if seqlens is None else [int(x) for x in seqlens]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            continue
+        rows = np.arange(n)
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            qs, ks, vs, dos = q[b, h, :n], k[b, kv, :n], v[b, kv, :n], do[b, h, :n]
+            s = scores_rows(qs, ks, scale, causal, rows)
+            if window is not None and window >= 0:
+                s = np.where(np.arange(n)[None, :] >= rows[:, None] - window, s, -np.inf)
+            p, _ = softmax_rows(s)
+            dp = dos @ vs.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, :n] = scale * (ds @ ks)
+            dk[b, kv, :n] += scale * (ds.T @ qs)
+            dv[b, kv, :n] += p.T @ dos
+    return dq, dk, dv
+
+
 def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
     """Attention of a few new queries against a KV cache.
 

@@ -435,7 +435,45 @@ def pin_masked_rows(impl):
         assert np.max(np.abs(lrow[fin] - lf[0, 0, rows][fin]), initial=0.0) < 1e-14
 
 
-MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows]
+def pin_masked_backward(impl):
+    """Central finite differences of sum(O * dO) through forward_masked; no
+    mask reduces to backward; padding rows and keys get zero gradients."""
+    rng = _rng(30)
+    h = 1e-6
+    for lens, window in (([6, 3], None), ([7, 7], 2), ([5, 0], 1)):
+        B, H, H_kv, N, d = 2, 2, 1, 7, 2
+        q = rng.standard_normal((B, H, N, d))
+        k = rng.standard_normal((B, H_kv, N, d))
+        v = rng.standard_normal((B, H_kv, N, d))
+        do = rng.standard_normal((B, H, N, d))
+        dq, dk, dv = impl.backward_masked(q, k, v, do, lens, window, 0.8, True)
+
+        def loss(qq, kk, vv):
+            o, _ = impl.forward_masked(qq, kk, vv, lens, window, 0.8, True)
+            return math.fsum((o * do).ravel().tolist())
+        for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy(); xp[idx] += h
+                xm = x.copy(); xm[idx] -= h
+                args = {"q": q, "k": k, "v": v}
+                lp = loss(*(xp if n == name else args[n] for n in "qkv"))
+                lm = loss(*(xm if n == name else args[n] for n in "qkv"))
+                num[idx] = (lp - lm) / (2 * h)
+            assert np.max(np.abs(num - gr)) < 1e-7, (name, lens, window)
+        for b, n in enumerate(lens):
+            assert np.all(dq[b, :, n:] == 0) and np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0)
+    q, k, v, do = (rng.standard_normal((2, 4, 9, 3)) if i != 1 and i != 2 else rng.standard_normal((2, 2, 9, 3))
+                   for i in range(4))
+    for causal in (False, True):
+        a = impl.backward(q, k, v, do, 0.5, causal)
+        m = impl.backward_masked(q, k, v, do, None, None, 0.5, causal)
+        for x, y in zip(a, m):
+            assert np.max(np.abs(x - y)) < 1e-13
+
+
+MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows,
+               pin_masked_backward]
 KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
                 pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]
 BACKWARD_PINS = [pin_finite_differences, pin_gradient_identities]

@@ -114,6 +114,39 @@ def test_masked_matches_torch_sdpa_fp64(case):
         assert np.max(np.abs(lse[b, :, :n] - torch.logsumexp(s, -1)[0].numpy())) < 1e-12
 
 
+@pytest.mark.parametrize("case", [(2, 4, 2, 40, 8, 9, True), (2, 4, 4, 33, 8, None, True),
+                                  (2, 2, 1, 30, 16, None, False)])
+def test_masked_backward_matches_torch_autograd_fp64(case):
+    """Library cross-check of backward_masked: torch autograd through CPU SDPA in
+    float64 on each unpadded sequence with the band mask."""
+    B, H, H_kv, N, d, window, causal = case
+    g = torch.Generator().manual_seed(3 * N + d)
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64)
+    do = torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    lens = [N, N // 2 + 1]
+    dq, dk, dv = oracle.backward_masked(q.numpy(), k.numpy(), v.numpy(), do.numpy(), lens, window, None, causal)
+    rep = H // H_kv
+    for b, n in enumerate(lens):
+        qq = q[b:b + 1, :, :n].clone().requires_grad_(True)
+        kk = k[b:b + 1, :, :n].clone().requires_grad_(True)
+        vv = v[b:b + 1, :, :n].clone().requires_grad_(True)
+        i, j = torch.arange(n)[:, None], torch.arange(n)[None, :]
+        mask = torch.ones(n, n, dtype=torch.bool)
+        if causal:
+            mask &= j <= i
+        if window is not None:
+            mask &= j >= i - window
+        out = F.scaled_dot_product_attention(qq, kk.repeat_interleave(rep, 1), vv.repeat_interleave(rep, 1),
+                                             attn_mask=mask)
+        out.backward(do[b:b + 1, :, :n])
+        assert np.max(np.abs(dq[b, :, :n] - qq.grad[0].numpy())) < 1e-11
+        assert np.max(np.abs(dk[b, :, :n] - kk.grad[0].numpy())) < 1e-11
+        assert np.max(np.abs(dv[b, :, :n] - vv.grad[0].numpy())) < 1e-11
+        assert np.all(dq[b, :, n:] == 0) and np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0)
+
+
 def _page_fp32_errors():
     path = os.path.join(os.path.dirname(__file__), "golden", "cpu_sdpa_fp32_error.txt")
     out = {}
@@ -168,6 +201,10 @@ MUTANTS = {
                           "s = np.where(cols > rows[:, None] - window, s, -np.inf)"),
     "window_ignored": ("s = np.where(cols >= rows[:, None] - window, s, -np.inf)", "s = s"),
     "padding_keys_kept": ("keys, vals = k[b, kv, :n], v[b, kv, :n]", "keys, vals = k[b, kv], v[b, kv]"),
+    "masked_bwd_no_window": ("                s = np.where(np.arange(n)[None, :] >= rows[:, None] - window, s, -np.inf)",
+                             "                s = s"),
+    "masked_bwd_ds_sign": ("            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))",
+                           "            ds = p * (np.sum(p * dp, axis=1, keepdims=True) - dp)"),
     "kvcache_v_whole_cache": ("o[b, h, rows] = p @ v[b, kv, :n]", "o[b, h, rows] = p @ v[b, kv, :p.shape[1]][::-1]"),
 }
 
