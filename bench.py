@@ -161,6 +161,23 @@ class MaskedCase:
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "window": self.w.window,
                 "valid_rows": int(sum(self.lens))}
 
+    def bwd_report(self, dev):
+        """Time the backward (dQ, dK, dV) of the same masked problem."""
+        import torch
+        import exact_tiled_attention_amd as fa
+        g = torch.Generator().manual_seed(self.w.seed + 1000)
+        do = torch.randn(self.o.shape, generator=g).to(torch.bfloat16).to(dev)
+        self.fwd()
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(self.w.B, self.w.H, self.w.H_kv, self.w.N, self.w.d, 1),
+                         device=dev, dtype=torch.uint8)
+        dq, dk, dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        fn = lambda: fa.fa_bwd_masked(self.q, self.k, self.v, self.o, self.lse, do, self.seqlens, self.w.window,
+                                      causal=self.w.causal, scale=self.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        ms = median(time_launches(fn, reps=5, warmup=1))
+        tf = 2.5 * self.w.flops_fwd(self.lens) / (ms * 1e-3) / 1e12
+        return {"kernel": f"bwd_bf16_d{self.w.d}_masked", "ms": round(ms, 4), "tflops": round(tf, 2),
+                "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -288,6 +305,7 @@ def main():
         c = MaskedCase(args.only, dev)
         xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
         rep = c.report(median(xs))
+        rep["bwd"] = c.bwd_report(dev)
         log(f"{args.only}: {rep}")
         print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
                           "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -372,6 +390,8 @@ def main():
             log(f"extra: {name}")
             c = MaskedCase(name, dev)
             extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
+            if name == "W1":
+                extra[name + ".bwd"] = c.bwd_report(dev)
             del c
             torch.cuda.empty_cache()
         for name in EXTRA_KV:

@@ -146,30 +146,32 @@ size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dty
   return 2 * row_stats;   // D = rowsum(dO * O), then LSE in base-2 units
 }
 
-fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-                 const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                 size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
-                 int causal, fa_dtype dtype, hipStream_t stream) {
+static fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                            const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                            size_t workspace_bytes, const int* seqlens, int window, int B, int H, int H_kv,
+                            int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL_POINTER;
   if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
   if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
   if (!fa_supported(dtype, d, 1)) return FA_ERR_UNSUPPORTED;
   if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
+  if (window >= 0 && !causal) return FA_ERR_INVALID_VALUE;
   const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
   for (const void* q : ptrs)
     if (!aligned16(q)) return FA_ERR_INVALID_VALUE;
+  if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return FA_ERR_INVALID_VALUE;
   const size_t need = fa_bwd_workspace_bytes(B, H, H_kv, N, d, dtype);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return FA_ERR_WORKSPACE;
   const size_t eb = elem_bytes(dtype);
   const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
   const size_t nl = (size_t)B * H * N * 4;
-  const void* ins[] = {Q, K, V, O, LSE, dO};
-  const size_t insz[] = {nq, nkv, nkv, nq, nl, nq};
+  const void* ins[] = {Q, K, V, O, LSE, dO, seqlens};
+  const size_t insz[] = {nq, nkv, nkv, nq, nl, nq, seqlens ? (size_t)B * 4 : 0};
   void* outs[] = {dQ, dK, dV, workspace};
   const size_t outsz[] = {nq, nkv, nkv, need};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_VALUE;
@@ -183,8 +185,26 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.seqlens = seqlens;
+  p.window = window < 0 ? -1 : window;
   const hipError_t e = fa::launch_bwd_bf16(d, causal != 0, p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                 size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
+                 int causal, fa_dtype dtype, hipStream_t stream) {
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, -1, B, H, H_kv, N,
+                    d, scale, causal, dtype, stream);
+}
+
+fa_status fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                        const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, const int* seqlens, int window, int B, int H, int H_kv,
+                        int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, seqlens, window, B, H, H_kv,
+                    N, d, scale, causal, dtype, stream);
 }
 
 int fa_kvcache_supported(fa_dtype dtype, int d) {

@@ -51,6 +51,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Valid rows of sequence b under a padding mask (N without one).
+template <bool MASK>
+__device__ __forceinline__ int valid_len(const BwdParams& p, int b) {
+  return MASK && p.seqlens ? min(max(p.seqlens[b], 0), p.N) : p.N;
+}
+// Zero gradient rows (bf16) for padding positions; lanes l and l ^ 32 each
+// write half of the row.
+__device__ __forceinline__ void zero_row(void* base, size_t row, int g, int d) {
+  bf16* r = (bf16*)base + row * d;
+  for (int c = 4 * g; c < d; c += 8) *(i32x2*)(r + c) = i32x2{0, 0};
+}
+
 // Offsets of the transposing read of a row-major tile: for 16-row block
 // base b (a multiple of 16), second = 0/1 selects rows b+0..7 / b+8..15 of the
 // block (4 rows per lane group), column block db selects 32 columns.  Lane i
@@ -80,7 +92,10 @@ struct DkdvCfg {
 // waves a SIMD a few values spill to scratch.  Measured on MI355X, that is
 // still faster than one wave a SIMD without spills (710 vs 649 TFLOP/s causal
 // at B=2, H=16, N=8192), so the instance keeps two waves.
-template <int D, bool CAUSAL>
+// With MASK (padding mask and/or sliding window, as in the forward) a key
+// block sees only the query tiles whose rows are valid and whose windows
+// reach it, and keys past the valid length get zero gradients.
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
@@ -91,7 +106,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap);
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap, p.group_items);
   const int kt = p.n_tiles - 1 - wi.qt;       // small key tiles (most queries) first
   const int N = p.N;
   const int bkv = wi.bh;                      // (b, kv head)
@@ -100,6 +115,15 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int k_first = kt * BKV;
   const int kw0 = k_first + wid * 32;         // this wave's first key
   const int mykey = kw0 + lr;                 // this lane's key (column of S)
+  const int L = valid_len<MASK>(p, b);
+  const int W = MASK ? p.window : -1;
+  if (MASK && k_first >= L) {                 // every key of the block is padding
+    if (mykey < N) {
+      zero_row(p.dk, (size_t)bkv * N + mykey, g, D);
+      zero_row(p.dv, (size_t)bkv * N + mykey, g, D);
+    }
+    return;
+  }
 
   const bf16* kgp = (const bf16*)p.k + (size_t)bkv * N * D;
   const bf16* vgp = (const bf16*)p.v + (size_t)bkv * N * D;
@@ -139,9 +163,11 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) troff[sec][db] = tr_off<RB>(lane, sec, db);
 
-  const int n_qt = (N + BQ - 1) / BQ;
+  const int n_qt = (L + BQ - 1) / BQ;        // tiles holding valid query rows
   const int qt_start = CAUSAL ? k_first / BQ : 0;
-  const int per_head = n_qt - qt_start;
+  // with a window, queries past the block's last key + W see none of it
+  const int qt_stop = MASK && W >= 0 ? min(n_qt, (k_first + BKV - 1 + W) / BQ + 1) : n_qt;
+  const int per_head = max(0, qt_stop - qt_start);
   const int n_iter = G * per_head;
   const float c = p.scale_log2;
 
@@ -150,7 +176,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int qt = qt_start + (it_idx - gi * per_head);
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
     const int row0 = qt * BQ;
-    const int rows = min(N - row0, BQ);
+    const int rows = min(L - row0, BQ);          // rows past the valid ones read as zero
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + (bh * N + row0) * D, rows * RB);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const bf16*)p.dout + (bh * N + row0) * D, rows * RB);
 #pragma unroll
@@ -176,6 +202,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qq0 = qrow0 + qb * 32;
       if (CAUSAL && qq0 + 31 < kw0) continue;   // every query precedes every key
+      if (MASK && (qq0 >= L || (W >= 0 && qq0 > kw0 + 31 + W))) continue;   // padding, or past every window
       // ---- S = Q K^T and dP = dO V^T (lane: key column, registers: query rows)
       f32x16 s = {}, dp = {};
 #pragma unroll
@@ -187,8 +214,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       // ---- P = exp2(S c - LSE2), dS = P (dP - D) -------------------------------
       // (the row statistics are read four rows at a time, as the registers use them)
-      const bool need_mask = CAUSAL && qq0 < kw0 + 31;
+      const bool need_mask = (CAUSAL && qq0 < kw0 + 31) ||
+                             (MASK && (qq0 + 31 >= L || (W >= 0 && qq0 + 31 > kw0 + W)));
       const int lim = mykey - qq0 - 4 * g;     // query row offset must be >= this
+      const int top = MASK ? min(L - 1, W >= 0 ? mykey + W : L - 1) - qq0 - 4 * g : 0;   // ... and <= this
       uint32_t pw[8], sw[8];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -201,7 +230,9 @@ void bwd_dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 2; ++e) {
             const int r = 4 * a4 + 2 * h2 + e;
             float pv = fast_exp2(fmaf(s[r], c, -lv[2 * h2 + e]));
-            if (need_mask && (8 * (r >> 2) + (r & 3)) < lim) pv = 0.f;
+            if (need_mask && ((CAUSAL && (8 * (r >> 2) + (r & 3)) < lim) ||
+                              (MASK && (8 * (r >> 2) + (r & 3)) > top)))
+              pv = 0.f;
             pe[e] = pv;
             se[e] = pv * (dp[r] - dvv[2 * h2 + e]);
           }
@@ -244,7 +275,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  if (mykey < N) {
+  if (MASK && mykey >= L) {
+    if (mykey < N) {
+      zero_row(p.dk, (size_t)bkv * N + mykey, g, D);
+      zero_row(p.dv, (size_t)bkv * N + mykey, g, D);
+    }
+  } else if (mykey < N) {
     bf16* dkr = (bf16*)p.dk + ((size_t)bkv * N + mykey) * D;
     bf16* dvr = (bf16*)p.dv + ((size_t)bkv * N + mykey) * D;
     const float sc = p.scale;
@@ -274,7 +310,7 @@ struct DqCfg {
   static_assert(IPW >= 1, "tile too small for the DMA split");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
@@ -285,13 +321,19 @@ void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap);
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap, p.group_items);
   const int N = p.N;
   const int b = wi.bh / p.H, h = wi.bh - b * p.H;
   const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
   const int q_first = wi.qt * BR;
   const int q0 = q_first + wid * 32;
   const int myq = q0 + lr;
+  const int L = valid_len<MASK>(p, b);
+  const int W = MASK ? p.window : -1;
+  if (MASK && q_first >= L) {                 // every row of the block is padding
+    if (myq < N) zero_row(p.dq, (size_t)wi.bh * N + myq, g, D);
+    return;
+  }
   const bf16* qgp = (const bf16*)p.q + (size_t)wi.bh * N * D;
   const bf16* dgp = (const bf16*)p.dout + (size_t)wi.bh * N * D;
   const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
@@ -309,7 +351,8 @@ void bwd_dq_kernel(BwdParams p) {
     qr[kb] = xq;
     dor[kb] = xd;
   }
-  const float lse2 = myq < N ? p.lse2[(size_t)wi.bh * N + myq] : 0.f;
+  // (a padding row takes P = 0 everywhere: its statistic reads as +inf)
+  const float lse2 = myq < L ? p.lse2[(size_t)wi.bh * N + myq] : (MASK ? INFINITY : 0.f);
   const float dlt = myq < N ? p.delta[(size_t)wi.bh * N + myq] : 0.f;
   const float c = p.scale_log2;
   f32x16 dq[D / 32];
@@ -332,12 +375,13 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) troff[sec][db] = tr_off<RB>(lane, sec, db);
 
-  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
+  const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
+  const int t0 = MASK && W >= 0 ? max(0, q_first - W) / BC : 0;   // tiles j = 0.. stand for t0 + j
+  const int n_tiles = (kv_end + BC - 1) / BC - t0;
 
   auto issue = [&](int j, unsigned char* st) {
-    const int key0 = j * BC;
-    const int bytes = min(N - key0, BC) * RB;
+    const int key0 = (t0 + j) * BC;
+    const int bytes = min(L - key0, BC) * RB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
 #pragma unroll
@@ -350,10 +394,13 @@ void bwd_dq_kernel(BwdParams p) {
   auto consume = [&](int j, const unsigned char* st) {
     const unsigned char* ks = st;
     const unsigned char* vs = st + C::KTILE;
-    const int key0 = j * BC;
+    const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;     // every key follows every row of the wave
-    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
-    const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+    if (MASK && W >= 0 && key0 + BC - 1 < q0 - W) return;   // below every row's window
+    const bool need_mask = (key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0) ||
+                           (MASK && W >= 0 && key0 < q0 + 31 - W);
+    const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
+    const int lo = MASK && W >= 0 ? myq - W - key0 - 4 * g : -BC;   // first visible key offset
     bf16x8 dsb[BC / 32][2];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
@@ -374,7 +421,9 @@ void bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * r2 + e;
           float pv = fast_exp2(fmaf(s[r], c, -lse2));
-          if (need_mask && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim) pv = 0.f;
+          if (need_mask && ((kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim ||
+                            (MASK && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) < lo)))
+            pv = 0.f;
           se[e] = pv * (dp[r] - dlt);
         }
         sw[r2] = pack_bf16(se[0], se[1]);
@@ -413,7 +462,9 @@ void bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  if (myq < N) {
+  if (MASK && myq >= L) {
+    if (myq < N) zero_row(p.dq, (size_t)wi.bh * N + myq, g, D);
+  } else if (myq < N) {
     bf16* dqr = (bf16*)p.dq + ((size_t)wi.bh * N + myq) * D;
     const float sc = p.scale;
 #pragma unroll
@@ -427,7 +478,7 @@ void bwd_dq_kernel(BwdParams p) {
 }
 
 // ========================================================= launchers ======
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
   {
     constexpr int RPB = 256 / (D / 8);
@@ -438,23 +489,30 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
     BwdParams q = p;
     q.n_tiles = (p.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
     q.total = p.B * p.H_kv * q.n_tiles;
-    q.remap = (q.total % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(q.total), dim3(DkdvCfg<D>::NT), 0, s, q);
+    q.group_items = q.n_tiles;                  // one (batch, K/V head) group per bh
+    q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, MASK>), dim3(q.total), dim3(DkdvCfg<D>::NT), 0, s, q);
   }
   {
     BwdParams q = p;
     q.n_tiles = (p.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
     q.total = p.B * p.H * q.n_tiles;
-    q.remap = (q.total % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(q.total), dim3(DqCfg<D>::NT), 0, s, q);
+    q.group_items = (p.H / p.H_kv) * q.n_tiles;
+    q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK>), dim3(q.total), dim3(DqCfg<D>::NT), 0, s, q);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(int d, bool causal, BwdParams& p, hipStream_t s) {
+  const bool m = p.seqlens != nullptr || p.window >= 0;
   switch (d) {
-    case 64: return causal ? launch_bwd<64, true>(p, s) : launch_bwd<64, false>(p, s);
-    case 128: return causal ? launch_bwd<128, true>(p, s) : launch_bwd<128, false>(p, s);
+    case 64:
+      if (m) return causal ? launch_bwd<64, true, true>(p, s) : launch_bwd<64, false, true>(p, s);
+      return causal ? launch_bwd<64, true, false>(p, s) : launch_bwd<64, false, false>(p, s);
+    case 128:
+      if (m) return causal ? launch_bwd<128, true, true>(p, s) : launch_bwd<128, false, true>(p, s);
+      return causal ? launch_bwd<128, true, false>(p, s) : launch_bwd<128, false, false>(p, s);
   }
   return hipErrorInvalidValue;
 }

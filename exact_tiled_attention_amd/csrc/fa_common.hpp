@@ -177,20 +177,29 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 // ----------------------------------------------------------- work map -----
 // Work item -> (head, q-tile).  Workgroups are handed to the 8 XCDs round
-// robin (id % 8), each XCD with its own L2.  When the item count divides by
-// 8 the map gives each XCD a contiguous range of items, so the q-tiles of one
-// head run on one XCD and share that head's K/V in its L2.  Inside a head the
-// heaviest causal tiles (largest q-tile index) are issued first.
+// robin (id % 8), each XCD with its own L2.  Items are numbered head-major,
+// and the heads of one (batch, K/V head) group -- group_items consecutive
+// items -- share that group's K/V.  The map keeps whole groups on one XCD so
+// they share its L2:
+//   remap 1  each XCD takes a contiguous eighth of the items;
+//   remap 2  XCD x takes groups x, x + 8, x + 16, ... (for sequences of
+//            different lengths, so that every XCD gets a mix of them);
+//   remap 0  no map (the counts do not divide by 8).
+// Inside a head the heaviest causal tiles (largest q-tile index) come first.
 struct WorkItem {
   int bh;
   int qt;
 };
-__device__ __forceinline__ WorkItem map_work(int block, int total, int n_qt, bool remap) {
-  int w = block;
-  if (remap) {
-    const int per = total >> 3;
-    w = (block & 7) * per + (block >> 3);
+// The item at position s of XCD x's share (total % 8 == 0).
+__device__ __forceinline__ int xcd_item(int x, int s, int total, int group_items, int remap) {
+  if (remap == 2) {
+    const int gl = s / group_items, within = s - gl * group_items;
+    return (x + 8 * gl) * group_items + within;
   }
+  return x * (total >> 3) + s;
+}
+__device__ __forceinline__ WorkItem map_work(int block, int total, int n_qt, int remap, int group_items) {
+  const int w = remap ? xcd_item(block & 7, block >> 3, total, group_items, remap) : block;
   WorkItem it;
   it.bh = w / n_qt;
   it.qt = n_qt - 1 - (w - it.bh * n_qt);
@@ -200,34 +209,41 @@ __device__ __forceinline__ WorkItem map_work(int block, int total, int n_qt, boo
 // Persistent grid: `workers` workgroups (one per CU) each loop over several
 // work items, so no workgroup ever waits for the dispatcher (which issues in
 // order and, with causal tiles of uneven length, stalls on a busy XCD while
-// other CUs idle).  The item list (head-major, heaviest causal tile of a head
-// first, as above) is split into 8 contiguous ranges, one per XCD when the
-// counts divide by 8 (workgroup b runs on XCD b % 8); inside its range,
-// worker c takes one item per round in snake order (c, then L-1-c, ...),
-// which balances uneven causal work and keeps an XCD on one or two heads.
+// other CUs idle).  With a map (remap != 0) each XCD's share of the items (as
+// above) is worked by that XCD's workers (workgroup b runs on XCD b % 8);
+// otherwise all workers share all items.  Worker c takes one item per round
+// in snake order (c, then L-1-c, ...), which balances uneven causal work and
+// keeps an XCD on one or two heads at a time.
 struct PersistentMap {
-  int base, per;   // item range of this worker's group of workers
-  int L, c;        // workers in the group, this worker's index in it
+  int x, per;      // XCD and size of this worker's share
+  int L, c;        // workers sharing it, this worker's index among them
+  int remap, group_items, total;
 };
-__device__ __forceinline__ PersistentMap persistent_map(int block, int workers, int total) {
+__device__ __forceinline__ PersistentMap persistent_map(int block, int workers, int total, int remap,
+                                                        int group_items) {
   PersistentMap m;
-  if (total % 8 == 0 && workers % 8 == 0) {
+  m.group_items = group_items;
+  m.total = total;
+  if (remap && total % 8 == 0 && workers % 8 == 0) {
+    m.x = block & 7;
     m.per = total >> 3;
-    m.base = (block & 7) * m.per;
     m.L = workers >> 3;
     m.c = block >> 3;
+    m.remap = remap;
   } else {
+    m.x = 0;
     m.per = total;
-    m.base = 0;
     m.L = workers;
     m.c = block;
+    m.remap = 0;
   }
   return m;
 }
 // Item of round r for this worker, or -1 when its share is done.
 __device__ __forceinline__ int persistent_item(const PersistentMap& m, int r) {
   const int j = r * m.L + ((r & 1) ? m.L - 1 - m.c : m.c);
-  return j < m.per ? m.base + j : -1;
+  if (j >= m.per) return -1;
+  return m.remap ? xcd_item(m.x, j, m.total, m.group_items, m.remap) : j;
 }
 __device__ __forceinline__ WorkItem item_of(int w, int n_qt) {
   WorkItem it;

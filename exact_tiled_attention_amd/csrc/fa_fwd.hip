@@ -377,14 +377,14 @@ template <int D, bool CAUSAL, bool FP8, bool PERSIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
   if constexpr (PERSIST) {
-    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total);
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
       fwd_mfma_kernel_item<D, CAUSAL, FP8>(p, item_of(w, p.n_qt));
     }
   } else {
-    fwd_mfma_kernel_item<D, CAUSAL, FP8>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    fwd_mfma_kernel_item<D, CAUSAL, FP8>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
   }
 }
 
@@ -641,7 +641,7 @@ template <int D, bool CAUSAL, int NW, int BC_, int NST, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdParams p) {
   if constexpr (PERSIST) {
-    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total);
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
@@ -649,7 +649,7 @@ void fwd_bf16_kernel(FwdParams p) {
       fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
   }
 }
 
@@ -984,7 +984,7 @@ template <int D, bool CAUSAL, int BC_, bool LATE, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pp_kernel(FwdParams p) {
   if constexpr (PERSIST) {
-    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total);
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
@@ -992,7 +992,7 @@ void fwd_bf16_pp_kernel(FwdParams p) {
       pp_item<D, CAUSAL, BC_, LATE, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    pp_item<D, CAUSAL, BC_, LATE, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    pp_item<D, CAUSAL, BC_, LATE, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
   }
 }
 
@@ -1305,7 +1305,7 @@ template <int D, bool CAUSAL, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pairs_kernel(FwdParams p) {
   if constexpr (PERSIST) {
-    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total);
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
     for (int r = 0;; ++r) {
       const int w = persistent_item(pm, r);
       if (w < 0) break;
@@ -1313,7 +1313,7 @@ void fwd_bf16_pairs_kernel(FwdParams p) {
       fwd_bf16_pairs_kernel_item<D, CAUSAL, MASK>(p, item_of(w, p.n_qt));
     }
   } else {
-    fwd_bf16_pairs_kernel_item<D, CAUSAL, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap));
+    fwd_bf16_pairs_kernel_item<D, CAUSAL, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
   }
 }
 
@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap);
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items);
   const int N = p.N;
   const int b = wi.bh / p.H, h = wi.bh - b * p.H;
   const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
@@ -1510,7 +1510,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(FwdParams p) {
 static void finish_grid(FwdParams& p, int br) {
   p.n_qt = (p.N + br - 1) / br;
   p.total = p.B * p.H * p.n_qt;
-  p.remap = (p.total % 8 == 0) ? 1 : 0;
+  // A contiguous eighth of the heads can be whole sequences; with a padding
+  // mask their lengths differ, so the (batch, K/V head) groups are dealt to
+  // the XCDs in turn instead.
+  const int groups = p.B * p.H_kv;
+  p.group_items = (p.H / p.H_kv) * p.n_qt;
+  p.remap = p.seqlens ? (groups % 8 == 0 ? 2 : 0) : (p.total % 8 == 0 ? 1 : 0);
 }
 
 // Compute units of the current device, read once per device.

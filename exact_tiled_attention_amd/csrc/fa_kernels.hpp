@@ -18,7 +18,8 @@ struct FwdParams {
   int B, H, H_kv, N;
   int n_qt;            // q-tiles per head
   int total;           // B * H * n_qt work items (= grid size)
-  int remap;           // 1: XCD-contiguous work map
+  int remap;           // XCD work map: 0 none, 1 contiguous, 2 groups dealt in turn
+  int group_items;     // items of one (batch, K/V head) group
   float scale_log2;    // scale * log2(e)
   const int* seqlens;  // [B] valid rows per sequence (padding mask), or null
   int window;          // causal sliding window: query i sees keys i - window .. i; < 0: none
@@ -42,9 +43,12 @@ struct BwdParams {
   int B, H, H_kv, N;
   int n_tiles;         // tiles per head of the kernel being launched
   int total;
-  int remap;
+  int remap;           // as in FwdParams
+  int group_items;
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
+  const int* seqlens;  // [B] valid rows per sequence (padding mask), or null
+  int window;          // causal sliding window as in FwdParams; < 0: none
 };
 
 // Attention of N_q new queries against a KV cache, split over the cache.

@@ -168,6 +168,19 @@ fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache
                          int H_kv, int N_q, int N_kv, int d, float scale, int causal, fa_dtype dtype,
                          hipStream_t stream);
 
+/*
+ * Backward of fa_fwd_masked (same seqlens and window, which must be the ones
+ * the forward used): arguments and workspace as in fa_bwd.  Gradient rows of
+ * padding positions (query rows and keys at or past seqlens[b]) are written
+ * as zero.  Supported: BF16 with d = 64, 128; FA_ERR_UNSUPPORTED otherwise;
+ * FA_ERR_INVALID_VALUE for window >= 0 without causal or a bad seqlens
+ * pointer.
+ */
+fa_status fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                        const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                        size_t workspace_bytes, const int* seqlens, int window, int B, int H, int H_kv,
+                        int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream);
+
 /* 1 if a kernel exists for (dtype, d, backward != 0), else 0. */
 int fa_supported(fa_dtype dtype, int d, int backward);
 

@@ -130,6 +130,18 @@ def test_masked_validation(lib):
     assert fwdm(lib, lse=4 * P + 64) == 4            # LSE inside O
 
 
+def test_masked_backward_validation(lib):
+    ptrs = [P * (i + 2) for i in range(9)]
+    def bwdm(seqlens=None, window=-1, d=64, dtype=1, causal=1):
+        return lib.fa_bwd_masked(*ptrs, 64 * P, 1 << 21, seqlens, window, 1, 2, 2, 16, d, 0.125, causal, dtype,
+                                 None)
+    assert bwdm(d=256) == 3
+    assert bwdm(dtype=0) == 3
+    assert bwdm(window=4, causal=0) == 4
+    assert bwdm(seqlens=70 * P + 1) == 4           # not 4-byte aligned
+    assert bwdm(seqlens=8 * P) == 4                # inside dQ
+
+
 def kvc(lib, q=P, k=2 * P, v=3 * P, kv_len=None, o=4 * P, lse=5 * P, ws=64 * P, ws_bytes=1 << 30,
         B=2, H=8, Hkv=2, Nq=1, Nkv=300, d=128, scale=0.08, causal=1, dtype=1):
     return lib.fa_fwd_kvcache(q, k, v, kv_len, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, scale,

@@ -129,3 +129,43 @@ def test_masked_full_size_sampled(name):
         o_ref, lse_ref = oracle.forward_masked_rows(x["q_64"][b, h], x["k_64"][b, kv], x["v_64"][b, kv], n,
                                                     w.window, x["scale"], w.causal, rows)
         _compare(o[b, h, rows], lse[b, h, rows], o_ref, lse_ref, what=(name, b, h))
+
+
+GRAD_TOL = 2e-2
+
+BWD_CASES = [
+    # B, H, H_kv, N, d, valid lengths, window, causal
+    (2, 4, 2, 300, 64, [300, 129], None, True),
+    (2, 4, 2, 300, 64, [300, 77], 100, True),
+    (2, 4, 4, 200, 64, [200, 31], None, False),
+    (2, 4, 2, 333, 128, [0, 333], 64, True),
+    (2, 8, 2, 300, 128, [300, 170], None, False),
+    (1, 4, 4, 400, 128, None, 200, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: f"{c[3]}x{c[4]}-w{c[6]}-{'c' if c[7] else 'nc'}")
+def test_masked_backward_small(case):
+    """Gradients through the masked kernels against the oracle's masked
+    backward; padding gradient rows must be exactly zero.  The tolerance is
+    2e-2 plus 2^-8 of the reference magnitude (one bf16 rounding of P and dS
+    on rows that see few keys), as for the plain backward's small shapes."""
+    B, H, H_kv, N, d, lens, window, causal = case
+    _say(f"masked backward {case}")
+    q, k, v, do = syn.draw(B, H, H_kv, N, d, 1.0, N + 7 * d + (window or 0), with_do=True)
+    x = syn.pack_inputs(q, k, v, do, "bf16")
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kd, vd, dod = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_masked(qd, kd, vd, sl, window, causal=causal)
+    dq, dk, dv = fa.fa_bwd_masked(qd, kd, vd, o, lse, dod, sl, window, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_masked(x["q_64"], x["k_64"], x["v_64"], x["do_64"], lens, window, x["scale"],
+                                        causal)
+    lens_ = [N] * B if lens is None else lens
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g64 = got.double().cpu().numpy()
+        tol = GRAD_TOL + 2.0 ** -8 * float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(g64 - ref)))
+        assert err <= tol, (case, name, err, tol)
+        for b, n in enumerate(lens_):
+            assert np.all(g64[b, :, n:] == 0.0), (case, name, b)
