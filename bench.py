@@ -400,6 +400,16 @@ def main():
             extra[name] = c.report(median(time_launches(c.fwd, reps=20, warmup=3)))
             del c
             torch.cuda.empty_cache()
+        for name in ("C2b", "C3"):
+            log(f"extra: {name} backward")
+            c = Case(name, dev, backward=True)
+            c.fwd()
+            ms_b = median(time_launches(c.bwd, reps=5, warmup=1))
+            tf = c.w.flops_bwd() / (ms_b * 1e-3) / 1e12
+            extra[name + ".bwd"] = {"kernel": kernel_name(c.w, "bwd"), "ms": round(ms_b, 4), "tflops": round(tf, 2),
+                                    "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+            del c
+            torch.cuda.empty_cache()
         log("extra: C4 forward + backward")
         c = Case("C4", dev, backward=True)
         ms_f = median(time_launches(c.fwd, reps=10, warmup=2))

@@ -46,7 +46,7 @@ extern "C" {
 
 int fa_supported(fa_dtype dtype, int d, int backward) {
   if (!valid_dtype(dtype)) return 0;
-  if (backward) return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128);
+  if (backward) return dtype == FA_DTYPE_BF16 && (d == 64 || d == 128 || d == 256);
   switch (dtype) {
     case FA_DTYPE_F32: return d == 64;
     case FA_DTYPE_BF16: return d == 64 || d == 128 || d == 256;

@@ -96,7 +96,7 @@ struct DkdvCfg {
 // block sees only the query tiles whose rows are valid and whose windows
 // reach it, and keys past the valid length get zero gradients.
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, RB = C::RB, IPW = C::IPW;
@@ -198,7 +198,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     const unsigned char* ds = st + C::QTILE;
     const float* lse2 = (const float*)(st + 2 * C::QTILE);
     const float* dl = lse2 + BQ;
-#pragma unroll
+    // (at d = 256 the two 32-query halves run one after the other: unrolled,
+    // their temporaries would not fit next to K, V, dK and dV)
+#pragma unroll (D > 128 ? 1 : BQ / 32)
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qq0 = qrow0 + qb * 32;
       if (CAUSAL && qq0 + 31 < kw0) continue;   // every query precedes every key
@@ -311,7 +313,7 @@ struct DqCfg {
 };
 
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void bwd_dq_kernel(BwdParams p) {
   using C = DqCfg<D>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW;
@@ -401,10 +403,9 @@ void bwd_dq_kernel(BwdParams p) {
                            (MASK && W >= 0 && key0 < q0 + 31 - W);
     const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
     const int lo = MASK && W >= 0 ? myq - W - key0 - 4 * g : -BC;   // first visible key offset
-    bf16x8 dsb[BC / 32][2];
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
-      // S^T = K Q^T and dP^T = V dO^T (lane: query column, registers: keys)
+    // dS^T of one 32-key block (lane: query column, registers: keys) ...
+    auto block_ds = [&](int kb32, bf16x8* ds2) __attribute__((always_inline)) {
+      // S^T = K Q^T and dP^T = V dO^T
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
@@ -430,22 +431,77 @@ void bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half)
-        dsb[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
-                                                           (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
-    }
-    // ---- dQ^T += K^T dS^T (K^T by transposing reads of the K rows) -----------
-#pragma unroll
-    for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+        ds2[half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
+                                                     (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
+    };
+    // ... and dQ^T += K^T dS^T for it (K^T by transposing reads of the K rows)
+    auto block_dq = [&](int kb32, const bf16x8* ds2) __attribute__((always_inline)) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int rb = (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo = lds_read_tr16(ks + rb + troff[0][db]);
-          const bf16x4 hi = lds_read_tr16(ks + rb + troff[1][db]);
-          dq[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kb32][half], dq[db]);
+          const bf16x4 lo4 = lds_read_tr16(ks + rb + troff[0][db]);
+          const bf16x4 hi4 = lds_read_tr16(ks + rb + troff[1][db]);
+          dq[db] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), ds2[half], dq[db]);
         }
       }
+    };
+    if constexpr (D > 128) {
+      // one block at a time: two blocks' temporaries do not fit next to Q, dO and dQ
+#pragma unroll 1
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+        bf16x8 ds2[2];
+        block_ds(kb32, ds2);
+        block_dq(kb32, ds2);
+      }
+    } else {
+      bf16x8 dsb[BC / 32][2];
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
+        // S^T = K Q^T and dP^T = V dO^T (lane: query column, registers: keys)
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) {
+          const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + roff[kb]);
+          const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + roff[kb]);
+          s = mfma_bf16(ak, qr[kb], s);
+          dp = mfma_bf16(av, dor[kb], dp);
+        }
+        uint32_t sw[8];
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+          float se[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * r2 + e;
+            float pv = fast_exp2(fmaf(s[r], c, -lse2));
+            if (need_mask && ((kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim ||
+                              (MASK && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) < lo)))
+              pv = 0.f;
+            se[e] = pv * (dp[r] - dlt);
+          }
+          sw[r2] = pack_bf16(se[0], se[1]);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          dsb[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
+                                                             (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
+      }
+      // ---- dQ^T += K^T dS^T (K^T by transposing reads of the K rows) ---------
+#pragma unroll
+      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int rb = (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x4 lo4 = lds_read_tr16(ks + rb + troff[0][db]);
+            const bf16x4 hi4 = lds_read_tr16(ks + rb + troff[1][db]);
+            dq[db] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kb32][half], dq[db]);
+          }
+        }
+    }
   };
 
   issue(0, stage0);
@@ -513,6 +569,11 @@ hipError_t launch_bwd_bf16(int d, bool causal, BwdParams& p, hipStream_t s) {
     case 128:
       if (m) return causal ? launch_bwd<128, true, true>(p, s) : launch_bwd<128, false, true>(p, s);
       return causal ? launch_bwd<128, true, false>(p, s) : launch_bwd<128, false, false>(p, s);
+    case 256:
+      // (without a mask the masked instances compute the same; the unmasked
+      // non-causal one spills a few registers and the masked one does not)
+      if (m || !causal) return causal ? launch_bwd<256, true, true>(p, s) : launch_bwd<256, false, true>(p, s);
+      return launch_bwd<256, true, false>(p, s);
   }
   return hipErrorInvalidValue;
 }

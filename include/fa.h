@@ -125,7 +125,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dty
  *   workspace: caller-owned device memory of at least
  *   fa_bwd_workspace_bytes(...) bytes, 256-byte aligned; its contents on
  *   entry do not matter and are garbage on return.
- * Supported: BF16 d=64,128.  FP8 has no backward (FA_ERR_UNSUPPORTED).
+ * Supported: BF16 d=64,128,256.  FP8 has no backward (FA_ERR_UNSUPPORTED).
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                  const void* dO, void* dQ, void* dK, void* dV, void* workspace,
@@ -172,7 +172,7 @@ fa_status fa_fwd_kvcache(const void* Q, const void* K_cache, const void* V_cache
  * Backward of fa_fwd_masked (same seqlens and window, which must be the ones
  * the forward used): arguments and workspace as in fa_bwd.  Gradient rows of
  * padding positions (query rows and keys at or past seqlens[b]) are written
- * as zero.  Supported: BF16 with d = 64, 128; FA_ERR_UNSUPPORTED otherwise;
+ * as zero.  Supported: BF16 with d = 64, 128, 256; FA_ERR_UNSUPPORTED otherwise;
  * FA_ERR_INVALID_VALUE for window >= 0 without causal or a bad seqlens
  * pointer.
  */

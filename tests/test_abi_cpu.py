@@ -57,9 +57,9 @@ def test_supported_table(lib):
     for d in (64, 128, 256):
         assert fa.fa_supported(1, d, False)
     assert fa.fa_supported(2, 128, False)
-    assert fa.fa_supported(1, 64, True) and fa.fa_supported(1, 128, True)
+    assert fa.fa_supported(1, 64, True) and fa.fa_supported(1, 128, True) and fa.fa_supported(1, 256, True)
     for dt, d, bwd in [(1, 96, False), (1, 192, False), (0, 128, False), (2, 64, False), (2, 128, True),
-                       (0, 64, True), (1, 256, True), (7, 64, False)]:
+                       (0, 64, True), (1, 96, True), (7, 64, False)]:
         assert not fa.fa_supported(dt, d, bwd), (dt, d, bwd)
 
 
@@ -102,7 +102,7 @@ def test_fwd_validation(lib):
 def test_bwd_validation(lib):
     assert bwd(lib, ptrs=[None] + [P * (i + 2) for i in range(8)]) == 1
     assert bwd(lib, dtype=2, d=128) == 3             # FP8 has no backward
-    assert bwd(lib, d=256) == 3
+    assert bwd(lib, d=96) == 3
     assert bwd(lib, N=0) == 2
     assert bwd(lib, scale=float("nan")) == 4
     assert bwd(lib, scale=-1.0) == 4
@@ -135,7 +135,7 @@ def test_masked_backward_validation(lib):
     def bwdm(seqlens=None, window=-1, d=64, dtype=1, causal=1):
         return lib.fa_bwd_masked(*ptrs, 64 * P, 1 << 21, seqlens, window, 1, 2, 2, 16, d, 0.125, causal, dtype,
                                  None)
-    assert bwdm(d=256) == 3
+    assert bwdm(d=96) == 3
     assert bwdm(dtype=0) == 3
     assert bwdm(window=4, causal=0) == 4
     assert bwdm(seqlens=70 * P + 1) == 4           # not 4-byte aligned

@@ -141,6 +141,8 @@ BWD_CASES = [
     (2, 4, 2, 333, 128, [0, 333], 64, True),
     (2, 8, 2, 300, 128, [300, 170], None, False),
     (1, 4, 4, 400, 128, None, 200, True),
+    (2, 4, 2, 300, 256, [300, 111], 70, True),
+    (2, 4, 4, 200, 256, [200, 57], None, False),
 ]
 
 

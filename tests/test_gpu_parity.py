@@ -166,7 +166,7 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 @pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 1)])
 def test_backward_small_shapes(d, causal, H, H_kv):
@@ -258,5 +258,37 @@ def test_full_size_fwd_bwd_c4():
         e = _err(got[b, h].double().cpu().numpy(), ref)
         _say(f"  C4 {name}: max abs err {e:.3e}")
         assert e <= GRAD_TOL, (name, e)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
+@pytest.mark.parametrize("wname", ["C2b", "C3"])
+def test_full_size_backward_one_group(wname):
+    """Backward at the d = 256 (C2b) and GQA prefill (C3) shapes: every dQ of the
+    query heads of one K/V group, and that group's dK and dV (summed over its
+    query heads), computed by the oracle one whole head at a time."""
+    w = syn.WORKLOADS[wname]
+    _say(f"full-size backward {w}")
+    x = syn.make_inputs(w, with_do=True)
+    q, k, v, do = (x[nm].to(DEV) for nm in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, causal=w.causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, do, causal=w.causal)
+    torch.cuda.synchronize()
+    b, kv = w.B - 1, w.H_kv - 1
+    g = w.H // w.H_kv
+    gk_sum = np.zeros_like(x["k_64"][b, kv])
+    gv_sum = np.zeros_like(x["v_64"][b, kv])
+    for h in range(kv * g, (kv + 1) * g):
+        gq, gk, gv, _, _ = oracle.backward_head(x["q_64"][b, h], x["k_64"][b, kv], x["v_64"][b, kv],
+                                                x["do_64"][b, h], x["scale"], w.causal)
+        e = _err(dq[b, h].double().cpu().numpy(), gq)
+        _say(f"  {wname} dQ head {h}: max abs err {e:.3e}")
+        assert e <= GRAD_TOL, (wname, "dQ", h, e)
+        gk_sum += gk
+        gv_sum += gv
+    for name, got, ref in (("dK", dk[b, kv], gk_sum), ("dV", dv[b, kv], gv_sum)):
+        e = _err(got.double().cpu().numpy(), ref)
+        _say(f"  {wname} {name}: max abs err {e:.3e}")
+        assert e <= GRAD_TOL, (wname, name, e)
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
