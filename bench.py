@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None, help="time one workload alone (profiling runs)")
+    ap.add_argument("--with-bwd", action="store_true", help="with --only: also run the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -315,7 +316,7 @@ def main():
         return
 
     names = [args.only] if args.only else STEP
-    cases = [Case(n, dev, backward=syn_workload(n).backward and bool(args.only)) for n in names]
+    cases = [Case(n, dev, backward=(syn_workload(n).backward or args.with_bwd) and bool(args.only)) for n in names]
     step_flops = sum(c.w.flops_fwd() + (c.w.flops_bwd() if c.backward else 0.0) for c in cases)
     log(f"timing {args.steps} steps of {names} after {args.warmup} warm-up steps")
 
