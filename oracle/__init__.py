@@ -28,6 +28,11 @@ from .attention import (  # noqa: F401
     forward_masked,
     forward_masked_rows,
     backward_masked,
+    block_mask_dense,
+    forward_dense_mask,
+    backward_dense_mask,
+    forward_blocksparse,
+    backward_blocksparse,
     visible_range,
     backward_head,
     backward,

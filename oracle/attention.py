@@ -205,6 +205,76 @@ def backward_masked(q, k, v, do, seqlens=None, window=None, scale=None, causal=T
     return dq, dk, dv
 
 
+def block_mask_dense(block_mask, n, block, causal):
+    """The [H, n, n] boolean key-visibility matrix of a block mask.
+
+    block_mask [H, nb, nb] (nonzero: query block qb sees key block kb) is
+    the block-sparse pattern of "FlashAttentionとは？…" (逆伝播でL×L行列を
+    保存せず再計算する設計: block-sparse FlashAttention at 64K); element (i, j)
+    is visible iff its block is on, and under the causal mask also j <= i.
+    """
+    bm = np.asarray(block_mask) != 0
+    idx = np.arange(n) // block
+    vis = bm[:, idx][:, :, idx]
+    if causal:
+        vis = vis & (np.arange(n)[None, :] <= np.arange(n)[:, None])[None]
+    return vis
+
+
+def forward_dense_mask(q, k, v, vis, scale=None):
+    """Attention with an explicit visibility matrix vis [H, N, N]; a row that
+    sees no key is O = 0, LSE = -inf."""
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((B, H, N, v.shape[3]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            rows = np.flatnonzero(vis[h].any(axis=1))
+            if rows.size == 0:
+                continue
+            s = np.where(vis[h][rows], scale * (q[b, h, rows] @ k[b, kv].T), -np.inf)
+            p, lse[b, h, rows] = softmax_rows(s)
+            o[b, h, rows] = p @ v[b, kv]
+    return o, lse
+
+
+def backward_dense_mask(q, k, v, do, vis, scale=None):
+    """Gradients of sum(O * dO) for forward_dense_mask (rows that see no key
+    contribute nothing)."""
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            kv = kv_head_of(h, H, H_kv)
+            rows = np.flatnonzero(vis[h].any(axis=1))
+            if rows.size == 0:
+                continue
+            s = np.where(vis[h][rows], scale * (q[b, h, rows] @ k[b, kv].T), -np.inf)
+            p, _ = softmax_rows(s)
+            dp = do[b, h, rows] @ v[b, kv].T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, rows] = scale * (ds @ k[b, kv])
+            dk[b, kv] += scale * (ds.T @ q[b, h, rows])
+            dv[b, kv] += p.T @ do[b, h, rows]
+    return dq, dk, dv
+
+
+def forward_blocksparse(q, k, v, block_mask, block=128, scale=None, causal=True):
+    """Block-sparse attention: forward_dense_mask of block_mask_dense."""
+    return forward_dense_mask(q, k, v, block_mask_dense(block_mask, q.shape[2], block, causal), scale)
+
+
+def backward_blocksparse(q, k, v, do, block_mask, block=128, scale=None, causal=True):
+    return backward_dense_mask(q, k, v, do, block_mask_dense(block_mask, q.shape[2], block, causal), scale)
+
+
 def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
     """Attention of a few new queries against a KV cache.
 

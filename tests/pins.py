@@ -472,7 +472,61 @@ def pin_masked_backward(impl):
             assert np.max(np.abs(x - y)) < 1e-13
 
 
-MASKED_PINS = [pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows,
+def pin_blocksparse(impl):
+    """All blocks on is plain attention; block-diagonal blocks are independent
+    attentions over each block; a scalar brute force; rows whose blocks are
+    all off (or all in the future) come back O = 0, LSE = -inf; gradients
+    match central finite differences."""
+    rng = _rng(31)
+    B, H, H_kv, N, d, blk = 2, 2, 1, 12, 3, 4
+    q = rng.standard_normal((B, H, N, d))
+    k, v = rng.standard_normal((B, H_kv, N, d)), rng.standard_normal((B, H_kv, N, d))
+    nb = N // blk
+    for causal in (False, True):
+        o0, l0 = impl.forward(q, k, v, 0.7, causal)
+        o1, l1 = impl.forward_blocksparse(q, k, v, np.ones((H, nb, nb)), blk, 0.7, causal)
+        assert np.max(np.abs(o1 - o0)) < 1e-14 and np.max(np.abs(l1 - l0)) < 1e-14
+        od, ld = impl.forward_blocksparse(q, k, v, np.stack([np.eye(nb)] * H), blk, 0.7, causal)
+        for bi in range(nb):
+            sl = slice(bi * blk, (bi + 1) * blk)
+            ob, lb = impl.forward(q[:, :, sl], k[:, :, sl], v[:, :, sl], 0.7, causal)
+            assert np.max(np.abs(od[:, :, sl] - ob)) < 1e-14 and np.max(np.abs(ld[:, :, sl] - lb)) < 1e-14
+    bm = rng.integers(0, 2, (H, nb, nb))
+    bm[0, 1, :] = 0                      # query block 1 of head 0 sees nothing
+    bm[1, 0, :] = 0
+    bm[1, 0, 2] = 1                      # only a future block: nothing under the causal mask
+    for causal in (False, True):
+        o, lse = impl.forward_blocksparse(q, k, v, bm, blk, 0.7, causal)
+        for b, h, i in itertools.product(range(B), range(H), range(N)):
+            js = [j for j in range(N) if bm[h, i // blk, j // blk] and (not causal or j <= i)]
+            if not js:
+                assert np.all(o[b, h, i] == 0) and lse[b, h, i] == -math.inf
+                continue
+            s_ = [0.7 * math.fsum(float(q[b, h, i, t]) * float(k[b, 0, j, t]) for t in range(d)) for j in js]
+            mx = max(s_)
+            w = [math.exp(x - mx) for x in s_]
+            tot = math.fsum(w)
+            assert abs(lse[b, h, i] - (mx + math.log(tot))) < 1e-13
+            for t in range(d):
+                assert abs(o[b, h, i, t] - math.fsum(wj * float(v[b, 0, j, t]) for wj, j in zip(w, js)) / tot) < 1e-13
+    do = rng.standard_normal(q.shape)
+    dq, dk, dv = impl.backward_blocksparse(q, k, v, do, bm, blk, 0.7, True)
+
+    def loss(qq, kk, vv):
+        o, _ = impl.forward_blocksparse(qq, kk, vv, bm, blk, 0.7, True)
+        return math.fsum((o * do).ravel().tolist())
+    hh = 1e-6
+    for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in list(np.ndindex(*x.shape))[::7]:
+            xp = x.copy(); xp[idx] += hh
+            xm = x.copy(); xm[idx] -= hh
+            args = {"q": q, "k": k, "v": v}
+            num = (loss(*(xp if n == name else args[n] for n in "qkv")) -
+                   loss(*(xm if n == name else args[n] for n in "qkv"))) / (2 * hh)
+            assert abs(num - gr[idx]) < 1e-7, (name, idx)
+
+
+MASKED_PINS = [pin_blocksparse, pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows,
                pin_masked_backward]
 KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
                 pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]

@@ -147,6 +147,38 @@ def test_masked_backward_matches_torch_autograd_fp64(case):
         assert np.all(dq[b, :, n:] == 0) and np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_matches_torch_sdpa_fp64(causal):
+    """Library cross-check of the block-sparse forward and backward: torch's CPU
+    SDPA and autograd in float64 with the block mask expanded here."""
+    B, H, H_kv, N, d, blk = 2, 4, 2, 40, 8, 8
+    g = torch.Generator().manual_seed(40 + causal)
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(B, H_kv, N, d, generator=g, dtype=torch.float64, requires_grad=True)
+    do = torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    nb = N // blk
+    bm = torch.randint(0, 2, (H, nb, nb), generator=g)
+    bm[:, torch.arange(nb), torch.arange(nb)] = 1          # every row sees its own block
+    mask = bm.repeat_interleave(blk, 1).repeat_interleave(blk, 2).bool()
+    if causal:
+        mask &= torch.ones(N, N, dtype=torch.bool).tril()
+    rep = H // H_kv
+    ref = F.scaled_dot_product_attention(q, k.repeat_interleave(rep, 1), v.repeat_interleave(rep, 1),
+                                         attn_mask=mask[None])
+    ref.backward(do)
+    o, lse = oracle.forward_blocksparse(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                                        bm.numpy(), blk, None, causal)
+    assert np.max(np.abs(o - ref.detach().numpy())) < 1e-12
+    s = (q @ k.repeat_interleave(rep, 1).transpose(-1, -2)).detach() / math.sqrt(d)
+    assert np.max(np.abs(lse - torch.logsumexp(s.masked_fill(~mask[None], float("-inf")), -1).numpy())) < 1e-12
+    dq, dk, dv = oracle.backward_blocksparse(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                                             do.numpy(), bm.numpy(), blk, None, causal)
+    assert np.max(np.abs(dq - q.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dk - k.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dv - v.grad.numpy())) < 1e-11
+
+
 def _page_fp32_errors():
     path = os.path.join(os.path.dirname(__file__), "golden", "cpu_sdpa_fp32_error.txt")
     out = {}
@@ -205,6 +237,10 @@ MUTANTS = {
                              "                s = s"),
     "masked_bwd_ds_sign": ("            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))",
                            "            ds = p * (np.sum(p * dp, axis=1, keepdims=True) - dp)"),
+    "blocksparse_transposed": ("    vis = bm[:, idx][:, :, idx]", "    vis = bm[:, idx][:, :, idx].transpose(0, 2, 1)"),
+    "blocksparse_no_causal": ("        vis = vis & (np.arange(n)[None, :] <= np.arange(n)[:, None])[None]", "        vis = vis"),
+    "dense_mask_empty_rows_nan": ("            rows = np.flatnonzero(vis[h].any(axis=1))\n            if rows.size == 0:\n                continue\n            s = np.where(vis[h][rows], scale * (q[b, h, rows] @ k[b, kv].T), -np.inf)\n            p, lse[b, h, rows]",
+                                  "            rows = np.arange(N)\n            if rows.size == 0:\n                continue\n            s = np.where(vis[h][rows], scale * (q[b, h, rows] @ k[b, kv].T), -np.inf)\n            p, lse[b, h, rows]"),
     "kvcache_v_whole_cache": ("o[b, h, rows] = p @ v[b, kv, :n]", "o[b, h, rows] = p @ v[b, kv, :p.shape[1]][::-1]"),
 }
 
