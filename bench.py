@@ -39,6 +39,7 @@ STEP = ["C2a", "C2a_nc", "C2b"]
 EXTRA_FWD = ["Ta", "Ta_gqa", "Tb", "Tc", "C1", "C3", "C5"]
 EXTRA_KV = ["D1", "D1_ragged"]
 EXTRA_MASKED = ["W1", "P1"]
+EXTRA_BLOCKSPARSE = ["S1"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_kvcache.hip", "fa_common.hpp")]
@@ -180,6 +181,50 @@ class MaskedCase:
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
 
 
+class BlockSparseCase:
+    """Device-resident inputs and block mask of one block-sparse workload."""
+
+    def __init__(self, name, dev):
+        import torch
+        import synthetic as syn
+        self.w = w = syn.BLOCKSPARSE_WORKLOADS[name]
+        x = syn.make_blocksparse_inputs(w)
+        self.bm_cpu = x["block_mask"]
+        self.scale = x["scale"]
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.bm = x["block_mask"].to(dev)
+        self.o = torch.empty(w.B, w.H, w.N, w.d, device=dev, dtype=torch.bfloat16)
+        self.lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
+
+    def fwd(self):
+        import exact_tiled_attention_amd as fa
+        fa.fa_fwd_blocksparse(self.q, self.k, self.v, self.bm, causal=self.w.causal, scale=self.scale,
+                              out=self.o, lse=self.lse)
+
+    def report(self, ms):
+        tf = self.w.flops_fwd(self.bm_cpu) / (ms * 1e-3) / 1e12
+        return {"kernel": f"fwd_bf16_d{self.w.d}_blocksparse", "ms": round(ms, 4), "tflops": round(tf, 2),
+                "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "block_density": self.w.density}
+
+    def bwd_report(self, dev):
+        """Time the backward (dQ, dK, dV) of the same block-sparse problem."""
+        import torch
+        import exact_tiled_attention_amd as fa
+        g = torch.Generator().manual_seed(self.w.seed + 1000)
+        do = torch.randn(self.o.shape, generator=g).to(torch.bfloat16).to(dev)
+        self.fwd()
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(self.w.B, self.w.H, self.w.H_kv, self.w.N, self.w.d, 1),
+                         device=dev, dtype=torch.uint8)
+        dq, dk, dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        fn = lambda: fa.fa_bwd_blocksparse(self.q, self.k, self.v, self.o, self.lse, do, self.bm,
+                                           causal=self.w.causal, scale=self.scale, workspace=ws,
+                                           dq=dq, dk=dk, dv=dv)
+        ms = median(time_launches(fn, reps=5, warmup=1))
+        tf = 2.5 * self.w.flops_fwd(self.bm_cpu) / (ms * 1e-3) / 1e12
+        return {"kernel": f"bwd_bf16_d{self.w.d}_blocksparse", "ms": round(ms, 4), "tflops": round(tf, 2),
+                "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -302,6 +347,18 @@ def main():
                           "config": {"workload": args.only}, "decode": rep}))
         return
 
+    if args.only in syn.BLOCKSPARSE_WORKLOADS:
+        c = BlockSparseCase(args.only, dev)
+        rep = c.report(median(time_launches(c.fwd, reps=args.steps, warmup=args.warmup)))
+        rep["bwd"] = c.bwd_report(dev)
+        log(f"{args.only}: {rep}")
+        print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
+                          "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": rep["ms"], "higher_is_better": True,
+                          "dtype": "bf16", "data": "synthetic", "config": {"workload": args.only},
+                          "blocksparse": rep}))
+        return
+
     if args.only in syn.MASKED_WORKLOADS:
         c = MaskedCase(args.only, dev)
         xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
@@ -393,6 +450,13 @@ def main():
             extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
             if name == "W1":
                 extra[name + ".bwd"] = c.bwd_report(dev)
+            del c
+            torch.cuda.empty_cache()
+        for name in EXTRA_BLOCKSPARSE:
+            log(f"extra: {name}")
+            c = BlockSparseCase(name, dev)
+            extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
+            extra[name]["bwd"] = c.bwd_report(dev)
             del c
             torch.cuda.empty_cache()
         for name in EXTRA_KV:

@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+__all__ = ["fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_masked", "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
            "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
            "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
 
@@ -25,7 +25,7 @@ FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE",
                 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_INVALID_VALUE", 5: "FA_ERR_WORKSPACE",
                 6: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+EXPORTED = ("fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_masked", "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
             "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
             "fa_status_string")
 
@@ -59,6 +59,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd.restype = i
     lib.fa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_masked.restype = i
+    lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_blocksparse.restype = i
+    lib.fa_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_blocksparse.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_supported.argtypes = [i, i, i]
@@ -285,5 +289,62 @@ def fa_bwd_masked(q, k, v, o, lse, do, seqlens=None, window: int | None = None, 
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _ptr(seqlens),
                              -1 if window is None else int(window), B, H, H_kv, N, d, float(scale),
                              int(bool(causal)), dt, _stream())
+    _check(code)
+    return dq, dk, dv
+
+
+def _block_mask_arg(block_mask, H, N):
+    torch = _torch()
+    nb = (N + 127) // 128
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous()
+            or tuple(block_mask.shape) != (H, nb, nb)):
+        raise ValueError(f"block_mask must be a contiguous uint8 device tensor of shape [{H}, {nb}, {nb}]")
+    return _ptr(block_mask)
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, causal: bool = True, scale: float | None = None,
+                       out=None, lse=None, want_lse: bool = True):
+    """O, LSE with a 128 x 128 block mask (uint8 device tensor [H, nb, nb])."""
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, N, d = _shape(q, k, v)
+    codes = DTYPE_CODES()
+    if q.dtype not in codes:
+        raise FaError(3, f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    bm = _block_mask_arg(block_mask, H, N)
+    if out is None:
+        out = torch.empty(B, H, N, d, device=q.device, dtype=torch.bfloat16)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    code = lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), bm, B, H, H_kv, N, d,
+                                  float(scale), int(bool(causal)), codes[q.dtype], _stream())
+    _check(code)
+    return out, lse
+
+
+def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = True, scale: float | None = None,
+                       workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV for fa_fwd_blocksparse with the same block mask."""
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, N, d = _shape(q, k, v)
+    codes = DTYPE_CODES()
+    if q.dtype not in codes:
+        raise FaError(3, f"unsupported dtype {q.dtype}")
+    dt = codes[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    bm = _block_mask_arg(block_mask, H, N)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    code = lib.fa_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(workspace), workspace.numel(), bm, B, H, H_kv, N, d,
+                                  float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv

@@ -140,6 +140,39 @@ fa_status fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, fl
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             const unsigned char* block_mask, int B, int H, int H_kv, int N, int d,
+                             float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !block_mask) return FA_ERR_NULL_POINTER;
+  if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
+  if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
+  if (dtype != FA_DTYPE_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_VALUE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FA_ERR_INVALID_VALUE;
+  const size_t nb = ((size_t)N + 127) / 128;
+  if (nb > 1024) return FA_ERR_INVALID_SHAPE;   // block masks cover N <= 131072
+  const size_t eb = elem_bytes(dtype);
+  const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
+  const size_t ob = nq, lb = LSE ? (size_t)B * H * N * 4 : 0, mb = (size_t)H * nb * nb;
+  const void* ins[] = {Q, K, V, block_mask};
+  const size_t insz[] = {nq, nkv, nkv, mb};
+  for (int j = 0; j < 4; ++j)
+    if (overlap(O, ob, ins[j], insz[j]) || overlap(LSE, lb, ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
+  if (overlap(LSE, lb, O, ob)) return FA_ERR_INVALID_VALUE;
+
+  fa::FwdParams p{};
+  p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.N = N;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.seqlens = nullptr;
+  p.window = -1;
+  p.block_mask = block_mask;
+  p.nb = (int)nb;
+  const hipError_t e = fa::launch_fwd_bf16(d, causal != 0, p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dtype) {
   if (!valid_dtype(dtype) || check_shape(B, H, H_kv, N, d) != FA_OK) return 0;
   const size_t row_stats = ((size_t)B * H * N * sizeof(float) + 255) & ~(size_t)255;
@@ -148,7 +181,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dty
 
 static fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                             const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                            size_t workspace_bytes, const int* seqlens, int window, int B, int H, int H_kv,
+                            size_t workspace_bytes, const int* seqlens, int window,
+                            const unsigned char* block_mask, int B, int H, int H_kv,
                             int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL_POINTER;
   if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
@@ -166,12 +200,14 @@ static fa_status bwd_common(const void* Q, const void* K, const void* V, const v
   const size_t eb = elem_bytes(dtype);
   const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
   const size_t nl = (size_t)B * H * N * 4;
-  const void* ins[] = {Q, K, V, O, LSE, dO, seqlens};
-  const size_t insz[] = {nq, nkv, nkv, nq, nl, nq, seqlens ? (size_t)B * 4 : 0};
+  const size_t nbk = ((size_t)N + 127) / 128;
+  const void* ins[] = {Q, K, V, O, LSE, dO, seqlens, block_mask};
+  const size_t insz[] = {nq, nkv, nkv, nq, nl, nq, seqlens ? (size_t)B * 4 : 0,
+                         block_mask ? (size_t)H * nbk * nbk : 0};
   void* outs[] = {dQ, dK, dV, workspace};
   const size_t outsz[] = {nq, nkv, nkv, need};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_VALUE;
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_VALUE;
@@ -187,6 +223,8 @@ static fa_status bwd_common(const void* Q, const void* K, const void* V, const v
   p.scale_log2 = scale * 1.4426950408889634f;
   p.seqlens = seqlens;
   p.window = window < 0 ? -1 : window;
+  p.block_mask = block_mask;
+  p.nb = (int)nbk;
   const hipError_t e = fa::launch_bwd_bf16(d, causal != 0, p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -195,16 +233,31 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                  size_t workspace_bytes, int B, int H, int H_kv, int N, int d, float scale,
                  int causal, fa_dtype dtype, hipStream_t stream) {
-  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, -1, B, H, H_kv, N,
-                    d, scale, causal, dtype, stream);
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, -1, nullptr, B, H,
+                    H_kv, N, d, scale, causal, dtype, stream);
 }
 
 fa_status fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                         const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                         size_t workspace_bytes, const int* seqlens, int window, int B, int H, int H_kv,
                         int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
-  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, seqlens, window, B, H, H_kv,
-                    N, d, scale, causal, dtype, stream);
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, seqlens, window, nullptr, B,
+                    H, H_kv, N, d, scale, causal, dtype, stream);
+}
+
+fa_status fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O,
+                             const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                             void* workspace, size_t workspace_bytes,
+                             const unsigned char* block_mask, int B, int H, int H_kv, int N, int d,
+                             float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+  if (!block_mask) return FA_ERR_NULL_POINTER;
+  if (valid_dtype(dtype) && d == 256) return FA_ERR_UNSUPPORTED;
+  // the flags of a key block's column for a GQA group fit 16 KB of LDS
+  if (H_kv > 0 && H % H_kv == 0 && N > 0 && ((size_t)N + 127) / 128 * (H / H_kv) > 16384)
+    return FA_ERR_INVALID_SHAPE;
+  if (N > 0 && ((size_t)N + 127) / 128 > 1024) return FA_ERR_INVALID_SHAPE;
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, -1, block_mask, B,
+                    H, H_kv, N, d, scale, causal, dtype, stream);
 }
 
 int fa_kvcache_supported(fa_dtype dtype, int d) {

@@ -56,6 +56,11 @@ template <bool MASK>
 __device__ __forceinline__ int valid_len(const BwdParams& p, int b) {
   return MASK && p.seqlens ? min(max(p.seqlens[b], 0), p.N) : p.N;
 }
+// Block-sparse: the flags a workgroup tests are copied to LDS once (each
+// tile then tests LDS instead of waiting on a global load): the dQ kernel's
+// row as bytes (nb <= 1024), the dK/dV kernel's column over a GQA group as
+// bits ((H / H_kv) * nb <= kMaxMaskBits), so its occupancy is unchanged.
+constexpr int kMaxMaskBits = 16384;
 // Zero gradient rows (bf16) for padding positions; lanes l and l ^ 32 each
 // write half of the row.
 __device__ __forceinline__ void zero_row(void* base, size_t row, int g, int d) {
@@ -171,7 +176,34 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int n_iter = G * per_head;
   const float c = p.scale_log2;
 
+  // Block-sparse: the key block is one 128-key block (BKV = 128); a query
+  // tile whose block is off for its head is neither loaded nor used (every
+  // wait here is for all loads).
+  static_assert(!MASK || BKV == 128, "block masks assume one key block per workgroup");
+  const bool bs = MASK && p.block_mask;
+  __shared__ unsigned long long bm_col[MASK ? kMaxMaskBits / 64 : 1];   // bit gi * nb + qb
+  if (bs) {
+    const int n = G * p.nb;
+    for (int base = 0; base < n; base += 256) {   // uniform trip count: every lane votes
+      const int i = base + tid;
+      bool on = false;
+      if (i < n) {
+        const int gi = i / p.nb, qb = i - gi * p.nb;
+        on = p.block_mask[((size_t)(kvh * G + gi) * p.nb + qb) * p.nb + (k_first >> 7)] != 0;
+      }
+      const unsigned long long bits = __ballot(on);
+      if ((tid & 63) == 0) bm_col[(base + tid) >> 6] = bits;
+    }
+    __syncthreads();
+  }
+  auto tile_on = [&](int it_idx) -> bool {
+    const int gi = it_idx / per_head;
+    const int qt = qt_start + (it_idx - gi * per_head);
+    const int bit = gi * p.nb + ((qt * BQ) >> 7);
+    return (bm_col[bit >> 6] >> (bit & 63)) & 1ull;
+  };
   auto issue = [&](int it_idx, unsigned char* st) {
+    if (bs && !tile_on(it_idx)) return;
     const int gi = it_idx / per_head;
     const int qt = qt_start + (it_idx - gi * per_head);
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
@@ -192,6 +224,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   auto consume = [&](int it_idx, const unsigned char* st) {
+    if (bs && !tile_on(it_idx)) return;
     const int gi = it_idx / per_head;
     const int qrow0 = (qt_start + (it_idx - gi * per_head)) * BQ;
     const unsigned char* qs = st;
@@ -381,8 +414,19 @@ void bwd_dq_kernel(BwdParams p) {
   const int t0 = MASK && W >= 0 ? max(0, q_first - W) / BC : 0;   // tiles j = 0.. stand for t0 + j
   const int n_tiles = (kv_end + BC - 1) / BC - t0;
 
+  // Block-sparse: the rows are one 128-row query block (BR = 128); a key
+  // tile whose block is off is neither loaded nor used.
+  static_assert(!MASK || BR == 128, "block masks assume one query block per workgroup");
+  const bool bs = MASK && p.block_mask;
+  __shared__ unsigned char bm_row[MASK ? 1024 : 1];
+  if (bs) {
+    for (int kb = tid; kb < p.nb; kb += 256)
+      bm_row[kb] = p.block_mask[((size_t)h * p.nb + (q_first >> 7)) * p.nb + kb];
+    __syncthreads();
+  }
   auto issue = [&](int j, unsigned char* st) {
     const int key0 = (t0 + j) * BC;
+    if (bs && !bm_row[key0 >> 7]) return;
     const int bytes = min(L - key0, BC) * RB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
@@ -399,6 +443,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;     // every key follows every row of the wave
     if (MASK && W >= 0 && key0 + BC - 1 < q0 - W) return;   // below every row's window
+    if (bs && !bm_row[key0 >> 7]) return;   // block off
     const bool need_mask = (key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0) ||
                            (MASK && W >= 0 && key0 < q0 + 31 - W);
     const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
@@ -561,7 +606,7 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_bf16(int d, bool causal, BwdParams& p, hipStream_t s) {
-  const bool m = p.seqlens != nullptr || p.window >= 0;
+  const bool m = p.seqlens != nullptr || p.window >= 0 || p.block_mask != nullptr;
   switch (d) {
     case 64:
       if (m) return causal ? launch_bwd<64, true, true>(p, s) : launch_bwd<64, false, true>(p, s);

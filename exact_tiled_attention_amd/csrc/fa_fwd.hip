@@ -85,8 +85,19 @@ __device__ __forceinline__ ItemMask mask_of(const FwdParams& p, int b, int q_fir
   }
   return m;
 }
-// O = 0 (bf16) and LSE = -inf for a padding row; lanes l and l ^ 32 each
-// write half of the row.
+// Block-sparse: a workgroup copies its query blocks' rows of the block mask
+// to LDS once per item (every tile then tests a byte there instead of
+// waiting on a global load); kMaxNb bounds a row (N <= 131072).
+constexpr int kMaxNb = 1024;
+__device__ __forceinline__ void stage_mask_rows(const FwdParams& p, int h, int qb, int rows,
+                                                unsigned char* dst) {
+  for (int i = threadIdx.x; i < rows * p.nb; i += blockDim.x) {
+    const int r = i / p.nb, kb = i - r * p.nb;
+    dst[r * kMaxNb + kb] = qb + r < p.nb ? p.block_mask[((size_t)h * p.nb + qb + r) * p.nb + kb] : 0;
+  }
+}
+// O = 0 (bf16) and LSE = -inf for a padding row, or a row that sees no key;
+// lanes l and l ^ 32 each write half of the row.
 __device__ __forceinline__ void write_empty_rows(const FwdParams& p, int bh, int myq, int g, int d) {
   if (myq >= p.N) return;
   bf16* orow = (bf16*)p.o + ((size_t)bh * p.N + myq) * d;
@@ -436,6 +447,15 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
   const int t0 = mk.t_begin;            // tiles j = 0.. stand for t0 + j
   const int n_tiles = (kv_end + BC - 1) / BC - t0;
+  // Block-sparse: the workgroup's rows are one 128-row query block
+  // (BR = 128); tiles whose key block is off are neither loaded nor used.
+  static_assert(!MASK || BR == 128, "block masks assume one query block per workgroup");
+  const bool bs = MASK && p.block_mask;
+  __shared__ unsigned char bm_row[MASK ? kMaxNb : 1];
+  if (bs) {
+    stage_mask_rows(p, h, q_first >> 7, 1, bm_row);
+    __syncthreads();
+  }
 
   // Q operand (B of S^T = K Q^T): slot (kb, g, e) <-> column kb*16 + 8g + e.
   bf16x8 qr[D / 16];
@@ -476,6 +496,8 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
 
   auto issue = [&](int j, unsigned char* st) {
     const int key0 = (t0 + j) * BC;
+    // (with two stages every wait is for all loads, so a tile can be left out)
+    if (NST == 2 && bs && !bm_row[key0 >> 7]) return;
     const int bytes = min(L - key0, BC) * RB;   // rows past the end read as zero
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
@@ -491,6 +513,7 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
     const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;   // every key of the tile follows every row of the wave
     if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return;   // below every row's window
+    if (bs && !bm_row[key0 >> 7]) return;                                     // block off
     f32x16 s[BC / 32];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
@@ -619,7 +642,7 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   }
 
   const float l_tot = sum_halves(l_run);
-  if (MASK && myq >= L) {
+  if (MASK && (myq >= L || l_tot == 0.f)) {   // padding, or a row that sees no key
     write_empty_rows(p, wi.bh, myq, g, D);
   } else if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -716,6 +739,17 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
   const int t0 = mk.t_begin;            // first key tile any row of the item sees
   const int n_tiles = (kv_end + BC - 1) / BC - t0;   // tiles j = 0.. stand for t0 + j
+  // Block-sparse: the item's two 128-row query blocks (waves 0-3 and 4-7).
+  const bool bs = MASK && p.block_mask;
+  __shared__ unsigned char bm_rows[MASK ? 2 * kMaxNb : 1];
+  if (bs) {
+    stage_mask_rows(p, h, q_first >> 7, 2, bm_rows);
+    __syncthreads();
+  }
+  const unsigned char* bm_wave = bm_rows + (wid >> 2) * kMaxNb;
+  auto tile_needed = [&](int key0) -> bool {   // by some wave of the item
+    return (bm_rows[key0 >> 7] | bm_rows[kMaxNb + (key0 >> 7)]) != 0;
+  };
 
   bf16x8 qr[D / 16];
 #pragma unroll
@@ -755,6 +789,9 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
 
   auto issue_one = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
     const int key0 = (t0 + j) * BC;
+    // (a tile no wave needs is not loaded; the LATE pipeline counts its loads,
+    // so there every tile is loaded)
+    if (!LATE && bs && !tile_needed(key0)) return;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(L - key0, BC) * RB);
 #pragma unroll
     for (int i = 0; i < IPD; ++i) dma16_buf<0>(r, off[i], st + (dwid * IPD + i) * 1024);
@@ -766,6 +803,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
     const int key0 = (t0 + j) * BC;
     if (CAUSAL && key0 > q0 + 31) return false;
     if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return false;   // below every row's window
+    if (bs && !bm_wave[key0 >> 7]) return false;                                  // block off for this wave
     // consecutive MFMAs go to different accumulators (no back-to-back chain)
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
@@ -958,7 +996,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   }
 
   const float l_tot = sum_halves(l_run);
-  if (MASK && myq >= L) {
+  if (MASK && (myq >= L || l_tot == 0.f)) {   // padding, or a row that sees no key
     write_empty_rows(p, wi.bh, myq, g, D);
   } else if (myq < N) {
     const float inv = 1.f / l_tot;

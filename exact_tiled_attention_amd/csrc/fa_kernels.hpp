@@ -23,10 +23,15 @@ struct FwdParams {
   float scale_log2;    // scale * log2(e)
   const int* seqlens;  // [B] valid rows per sequence (padding mask), or null
   int window;          // causal sliding window: query i sees keys i - window .. i; < 0: none
+  const unsigned char* block_mask;   // [H][nb][nb] 128 x 128 block mask, or null
+  int nb;              // ceil(N / 128)
 };
 
-// True when a forward call carries a padding mask or a sliding window.
-inline bool masked(const FwdParams& p) { return p.seqlens != nullptr || p.window >= 0; }
+// True when a forward call carries a padding mask, a sliding window or a
+// block mask.
+inline bool masked(const FwdParams& p) {
+  return p.seqlens != nullptr || p.window >= 0 || p.block_mask != nullptr;
+}
 
 struct BwdParams {
   const void* q;
@@ -49,6 +54,8 @@ struct BwdParams {
   float scale_log2;    // scale * log2(e)
   const int* seqlens;  // [B] valid rows per sequence (padding mask), or null
   int window;          // causal sliding window as in FwdParams; < 0: none
+  const unsigned char* block_mask;   // as in FwdParams
+  int nb;
 };
 
 // Attention of N_q new queries against a KV cache, split over the cache.

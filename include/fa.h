@@ -111,6 +111,37 @@ fa_status fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, fl
                         float scale, int causal, fa_dtype dtype, hipStream_t stream);
 
 /*
+ * Block-sparse forward: a 128 x 128 block mask decides which (query block,
+ * key block) pairs are computed -- the block-sparse variant of FlashAttention
+ * that "FlashAttentionとは？…" reports for 64K sequences (subsection
+ * 逆伝播でL×L行列を保存せず再計算する設計).  Arguments as in fa_fwd (bf16, no
+ * descales), plus:
+ *   block_mask: DEVICE uint8 [H][nb][nb], nb = ceil(N / 128), shared by every
+ *     sequence of the batch; a nonzero byte lets query block qb of head h see
+ *     key block kb.  Query i sees key j iff block (i / 128, j / 128) is on
+ *     and, when causal, j <= i.  A row that sees no key gets O = 0,
+ *     LSE = -inf.  Key tiles whose blocks are off are neither loaded nor
+ *     computed.
+ * Supported: BF16 with d = 64, 128 (FA_ERR_UNSUPPORTED otherwise) and
+ * N <= 131072 (FA_ERR_INVALID_SHAPE otherwise: a workgroup keeps its rows of
+ * the mask in on-chip memory).
+ */
+fa_status fa_fwd_blocksparse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             const unsigned char* block_mask, int B, int H, int H_kv, int N, int d,
+                             float scale, int causal, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Backward of fa_fwd_blocksparse (the same block mask): arguments and
+ * workspace as in fa_bwd.  Supported: BF16 with d = 64, 128, N <= 131072 and
+ * (H / H_kv) * ceil(N / 128) <= 16384.
+ */
+fa_status fa_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O,
+                             const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                             void* workspace, size_t workspace_bytes,
+                             const unsigned char* block_mask, int B, int H, int H_kv, int N, int d,
+                             float scale, int causal, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for this problem (0 on invalid
  * arguments).  The workspace holds two fp32 [B][H][N] arrays: D = rowsum(dO * O)
  * and the forward's LSE in base-2 units.

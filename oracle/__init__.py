@@ -32,6 +32,7 @@ from .attention import (  # noqa: F401
     forward_dense_mask,
     backward_dense_mask,
     forward_blocksparse,
+    forward_blocksparse_rows,
     backward_blocksparse,
     visible_range,
     backward_head,

@@ -275,6 +275,28 @@ def backward_blocksparse(q, k, v, do, block_mask, block=128, scale=None, causal=
     return backward_dense_mask(q, k, v, do, block_mask_dense(block_mask, q.shape[2], block, causal), scale)
 
 
+def forward_blocksparse_rows(q, k, v, block_mask, block, scale, causal, rows):
+    """Selected query rows of one head of forward_blocksparse (q [N,d], k/v
+    [N,d], block_mask [nb, nb] of that head), one row at a time."""
+    bm = np.asarray(block_mask) != 0
+    n = k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.zeros((rows.size, v.shape[1]))
+    lse = np.full(rows.size, -np.inf)
+    kblock = np.arange(n) // block
+    for t, i in enumerate(rows):
+        vis = bm[i // block][kblock]
+        if causal:
+            vis = vis & (np.arange(n) <= i)
+        js = np.flatnonzero(vis)
+        if js.size == 0:
+            continue
+        p, l = softmax_rows((scale * (k[js] @ q[i]))[None, :])
+        o[t] = p[0] @ v[js]
+        lse[t] = l[0]
+    return o, lse
+
+
 def forward_kvcache(q, k, v, kv_len=None, scale=None, causal=True):
     """Attention of a few new queries against a KV cache.
 

@@ -310,3 +310,77 @@ def make_masked_inputs(w: MaskedWorkload):
     out["seqlens"] = cache_lengths(w.B, w.N, w.seed) if w.ragged else None
     out["lens"] = out["seqlens"].tolist() if w.ragged else [w.N] * w.B
     return out
+
+
+# ------------------------------------------------------------- block-sparse ---
+
+@dataclass(frozen=True)
+class BlockSparseWorkload:
+    """A forward with a 128 x 128 block mask per head: each block is on with
+    probability ``density`` (seeded), and the diagonal blocks are always on
+    so that every query sees at least itself."""
+
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    N: int
+    d: int
+    density: float
+    dtype: str = "bf16"
+    causal: bool = True
+    amp: float = 1.0
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    def visible_pairs(self, block_mask) -> int:
+        """(query, key) pairs the mask leaves, summed over heads (per sequence)."""
+        nb = block_mask.shape[1]
+        bm = block_mask.to(torch.int64)
+        if not self.causal:
+            return int(bm.sum()) * 128 * 128 if self.N % 128 == 0 else _pairs_exact(bm, self.N, False)
+        return _pairs_exact(bm, self.N, True)
+
+    def flops_fwd(self, block_mask) -> float:
+        return 4.0 * self.B * self.d * self.visible_pairs(block_mask)
+
+
+def _pairs_exact(bm, n, causal):
+    """Visible pairs of a block mask over n tokens, summed over heads."""
+    nb = bm.shape[1]
+    size = torch.full((nb,), 128, dtype=torch.int64)
+    size[-1] = n - 128 * (nb - 1)
+    full = size[:, None] * size[None, :]                   # pairs per block
+    if causal:
+        strict = torch.ones(nb, nb, dtype=torch.bool).tril(-1)
+        diag = size * (size + 1) // 2                       # a diagonal block's lower triangle
+        per = torch.where(strict, full, torch.zeros_like(full))
+        per = per + torch.diag(diag)
+    else:
+        per = full
+    return int((bm * per[None]).sum())
+
+
+def block_mask(w: BlockSparseWorkload):
+    """Seeded uint8 CPU tensor [H, nb, nb] of the workload's block mask."""
+    nb = (w.N + 127) // 128
+    g = torch.Generator("cpu").manual_seed(w.seed + 31337)
+    m = (torch.rand(w.H, nb, nb, generator=g) < w.density).to(torch.uint8)
+    idx = torch.arange(nb)
+    m[:, idx, idx] = 1
+    return m
+
+
+# The block-sparse setting of the pages' 64K experiment, at the head layout of
+# the GQA prefill shape with d = 128; seed 14.
+BLOCKSPARSE_WORKLOADS = {
+    "S1": BlockSparseWorkload("S1", 1, 16, 4, 65536, 128, 0.25, seed=14,
+                              note="causal, 25% of the 128x128 blocks on (diagonal always on)"),
+}
+
+
+def make_blocksparse_inputs(w: BlockSparseWorkload):
+    q, k, v, _ = draw(w.B, w.H, w.H_kv, w.N, w.d, w.amp, w.seed)
+    out = pack_inputs(q, k, v, None, w.dtype)
+    out["block_mask"] = block_mask(w)
+    return out

@@ -526,7 +526,25 @@ def pin_blocksparse(impl):
             assert abs(num - gr[idx]) < 1e-7, (name, idx)
 
 
-MASKED_PINS = [pin_blocksparse, pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows,
+def pin_blocksparse_rows(impl):
+    """Row subsets of one head agree with the whole computation."""
+    rng = _rng(32)
+    q = rng.standard_normal((1, 2, 24, 3))
+    k, v = rng.standard_normal((1, 1, 24, 3)), rng.standard_normal((1, 1, 24, 3))
+    bm = rng.integers(0, 2, (2, 4, 4))
+    bm[1, 2, :] = 0
+    rows = [0, 5, 13, 14, 23]
+    for causal in (False, True):
+        of, lf = impl.forward_blocksparse(q, k, v, bm, 6, 0.9, causal)
+        for h in range(2):
+            orow, lrow = impl.forward_blocksparse_rows(q[0, h], k[0, 0], v[0, 0], bm[h], 6, 0.9, causal, rows)
+            assert np.max(np.abs(orow - of[0, h, rows])) < 1e-14
+            fin = np.isfinite(lf[0, h, rows])
+            assert np.array_equal(np.isfinite(lrow), fin)
+            assert np.max(np.abs(lrow[fin] - lf[0, h, rows][fin]), initial=0.0) < 1e-14
+
+
+MASKED_PINS = [pin_blocksparse, pin_blocksparse_rows, pin_masked_brute_force, pin_masked_reductions, pin_masked_window_closed_forms, pin_masked_rows,
                pin_masked_backward]
 KVCACHE_PINS = [pin_kvcache_brute_force, pin_kvcache_square_case, pin_kvcache_tail_ignored,
                 pin_kvcache_identical_keys, pin_kvcache_last_query_sees_all]

@@ -142,6 +142,24 @@ def test_masked_backward_validation(lib):
     assert bwdm(seqlens=8 * P) == 4                # inside dQ
 
 
+def test_blocksparse_validation(lib):
+    f = lambda bm=9 * P, d=64, dtype=1, o=4 * P, N=16: lib.fa_fwd_blocksparse(
+        P, 2 * P, 3 * P, o, 5 * P, bm, 1, 2, 2, N, d, 0.125, 1, dtype, None)
+    assert f(bm=None) == 1
+    assert f(d=256) == 3                             # no d = 256 block-sparse kernel
+    assert f(dtype=0) == 3
+    assert f(bm=4 * P + 64) == 4                     # mask inside O
+    assert f(N=131073) == 2                          # a mask row is at most 1024 blocks
+    ptrs = [P * (i + 2) for i in range(9)]
+    g = lambda bm=70 * P, d=64, H=2, Hkv=2, N=16: lib.fa_bwd_blocksparse(
+        *ptrs, 64 * P, 1 << 40, bm, 1, H, Hkv, N, d, 0.125, 1, 1, None)
+    assert g(bm=None) == 1
+    assert g(d=256) == 3
+    assert g(bm=8 * P) == 4                          # mask inside dQ
+    assert g(N=131073) == 2
+    assert g(H=32, Hkv=1, N=65536 + 1) == 2          # a GQA group's key-block column over 16384 flags
+
+
 def kvc(lib, q=P, k=2 * P, v=3 * P, kv_len=None, o=4 * P, lse=5 * P, ws=64 * P, ws_bytes=1 << 30,
         B=2, H=8, Hkv=2, Nq=1, Nkv=300, d=128, scale=0.08, causal=1, dtype=1):
     return lib.fa_fwd_kvcache(q, k, v, kv_len, o, lse, ws, ws_bytes, B, H, Hkv, Nq, Nkv, d, scale,
