@@ -56,11 +56,19 @@ template <bool MASK>
 __device__ __forceinline__ int valid_len(const BwdParams& p, int b) {
   return MASK && p.seqlens ? min(max(p.seqlens[b], 0), p.N) : p.N;
 }
-// Block-sparse: the flags a workgroup tests are copied to LDS once (each
-// tile then tests LDS instead of waiting on a global load): the dQ kernel's
-// row as bytes (nb <= 1024), the dK/dV kernel's column over a GQA group as
-// bits ((H / H_kv) * nb <= kMaxMaskBits), so its occupancy is unchanged.
+// Block-sparse: the dK/dV kernel keeps its key block's column of the mask
+// over a GQA group in LDS as bits ((H / H_kv) * nb <= kMaxMaskBits: 2 KB,
+// so its occupancy is unchanged) and steps from one set bit's query tiles
+// to the next; the dQ kernel runs over a list of its key tiles that are on.
 constexpr int kMaxMaskBits = 16384;
+// A 64-bit LDS word every lane of the wave reads at one address, made
+// scalar (so loops over it stay uniform).
+__device__ __forceinline__ unsigned long long lds_u64_uniform(const unsigned long long* a) {
+  const unsigned long long w = *a;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)w);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(w >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
 // Zero gradient rows (bf16) for padding positions; lanes l and l ^ 32 each
 // write half of the row.
 __device__ __forceinline__ void zero_row(void* base, size_t row, int g, int d) {
@@ -176,34 +184,48 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int n_iter = G * per_head;
   const float c = p.scale_log2;
 
-  // Block-sparse: the key block is one 128-key block (BKV = 128); a query
-  // tile whose block is off for its head is neither loaded nor used (every
-  // wait here is for all loads).
+  // Block-sparse: the key block is one 128-key block (BKV = 128).  Bit
+  // gi * nb + qb is set when query block qb of group head gi has it on and
+  // holds some of the tiles [qt_start, qt_stop); steps in the order of
+  // it_idx (gi major) then visit only the tiles of set bits.
   static_assert(!MASK || BKV == 128, "block masks assume one key block per workgroup");
+  static_assert(128 % BQ == 0, "query tiles split a mask block");
   const bool bs = MASK && p.block_mask;
-  __shared__ unsigned long long bm_col[MASK ? kMaxMaskBits / 64 : 1];   // bit gi * nb + qb
+  __shared__ unsigned long long bm_col[MASK ? kMaxMaskBits / 64 : 1];
+  const int n_bits = G * p.nb;
   if (bs) {
-    const int n = G * p.nb;
-    for (int base = 0; base < n; base += 256) {   // uniform trip count: every lane votes
+    for (int base = 0; base < n_bits; base += 256) {   // uniform trip count: every lane votes
       const int i = base + tid;
       bool on = false;
-      if (i < n) {
+      if (i < n_bits) {
         const int gi = i / p.nb, qb = i - gi * p.nb;
-        on = p.block_mask[((size_t)(kvh * G + gi) * p.nb + qb) * p.nb + (k_first >> 7)] != 0;
+        on = qb * (128 / BQ) < qt_stop && (qb + 1) * (128 / BQ) > qt_start &&
+             p.block_mask[((size_t)(kvh * G + gi) * p.nb + qb) * p.nb + (k_first >> 7)] != 0;
       }
       const unsigned long long bits = __ballot(on);
       if ((tid & 63) == 0) bm_col[(base + tid) >> 6] = bits;
     }
     __syncthreads();
   }
-  auto tile_on = [&](int it_idx) -> bool {
-    const int gi = it_idx / per_head;
-    const int qt = qt_start + (it_idx - gi * per_head);
+  // first step >= it whose tile is on (n_iter if none)
+  auto next_on = [&](int it) -> int {
+    if (!bs || it >= n_iter) return it;
+    const int gi = it / per_head;
+    const int qt = qt_start + (it - gi * per_head);
     const int bit = gi * p.nb + ((qt * BQ) >> 7);
-    return (bm_col[bit >> 6] >> (bit & 63)) & 1ull;
+    int word = bit >> 6;
+    unsigned long long w = lds_u64_uniform(bm_col + word);
+    if ((w >> (bit & 63)) & 1ull) return it;
+    w &= (~0ull << (bit & 63)) << 1;                     // the bits after this block's
+    while (w == 0) {
+      if (++word >= (n_bits + 63) >> 6) return n_iter;
+      w = lds_u64_uniform(bm_col + word);
+    }
+    const int nbit = word * 64 + __builtin_ctzll(w);
+    const int gi2 = nbit / p.nb, qb2 = nbit - gi2 * p.nb;
+    return gi2 * per_head + max(qb2 * (128 / BQ), qt_start) - qt_start;
   };
   auto issue = [&](int it_idx, unsigned char* st) {
-    if (bs && !tile_on(it_idx)) return;
     const int gi = it_idx / per_head;
     const int qt = qt_start + (it_idx - gi * per_head);
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
@@ -224,7 +246,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   auto consume = [&](int it_idx, const unsigned char* st) {
-    if (bs && !tile_on(it_idx)) return;
     const int gi = it_idx / per_head;
     const int qrow0 = (qt_start + (it_idx - gi * per_head)) * BQ;
     const unsigned char* qs = st;
@@ -296,17 +317,38 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  if (n_iter > 0) issue(0, stage0);
-  for (int it = 0; it < n_iter; it += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < n_iter) issue(it + 1, stage1);
-    consume(it, stage0);
-    if (it + 1 < n_iter) {
+  if constexpr (MASK) {
+    // (without a block mask the steps are 0, 1, .., n_iter - 1)
+    int cur = next_on(0);
+    if (cur < n_iter) issue(cur, stage0);
+    while (cur < n_iter) {
+      int nxt = next_on(cur + 1);
       wait_vmem();
       __syncthreads();
-      if (it + 2 < n_iter) issue(it + 2, stage0);
-      consume(it + 1, stage1);
+      if (nxt < n_iter) issue(nxt, stage1);
+      consume(cur, stage0);
+      cur = nxt;
+      if (cur >= n_iter) break;
+      nxt = next_on(cur + 1);
+      wait_vmem();
+      __syncthreads();
+      if (nxt < n_iter) issue(nxt, stage0);
+      consume(cur, stage1);
+      cur = nxt;
+    }
+  } else {
+    if (n_iter > 0) issue(0, stage0);
+    for (int it = 0; it < n_iter; it += 2) {
+      wait_vmem();
+      __syncthreads();
+      if (it + 1 < n_iter) issue(it + 1, stage1);
+      consume(it, stage0);
+      if (it + 1 < n_iter) {
+        wait_vmem();
+        __syncthreads();
+        if (it + 2 < n_iter) issue(it + 2, stage0);
+        consume(it + 1, stage1);
+      }
     }
   }
 
@@ -412,21 +454,20 @@ void bwd_dq_kernel(BwdParams p) {
 
   const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
   const int t0 = MASK && W >= 0 ? max(0, q_first - W) / BC : 0;   // tiles j = 0.. stand for t0 + j
-  const int n_tiles = (kv_end + BC - 1) / BC - t0;
+  int n_tiles = (kv_end + BC - 1) / BC - t0;
 
-  // Block-sparse: the rows are one 128-row query block (BR = 128); a key
-  // tile whose block is off is neither loaded nor used.
+  // Block-sparse: the rows are one 128-row query block (BR = 128); step j
+  // takes the j-th tile of the list of key tiles that are on.
   static_assert(!MASK || BR == 128, "block masks assume one query block per workgroup");
   const bool bs = MASK && p.block_mask;
-  __shared__ unsigned char bm_row[MASK ? 1024 : 1];
-  if (bs) {
-    for (int kb = tid; kb < p.nb; kb += 256)
-      bm_row[kb] = p.block_mask[((size_t)h * p.nb + (q_first >> 7)) * p.nb + kb];
-    __syncthreads();
-  }
+  __shared__ unsigned short tlist[MASK ? kMaxTiles : 1];
+  __shared__ int tcount;
+  if (bs) n_tiles = list_tiles<BC, 1>(p.block_mask, p.nb, h, q_first >> 7, t0, n_tiles, tlist, &tcount);
+  auto tile_of = [&](int j) -> int {
+    return bs ? __builtin_amdgcn_readfirstlane((int)tlist[j]) >> 2 : t0 + j;
+  };
   auto issue = [&](int j, unsigned char* st) {
-    const int key0 = (t0 + j) * BC;
-    if (bs && !bm_row[key0 >> 7]) return;
+    const int key0 = tile_of(j) * BC;
     const int bytes = min(L - key0, BC) * RB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
@@ -440,10 +481,9 @@ void bwd_dq_kernel(BwdParams p) {
   auto consume = [&](int j, const unsigned char* st) {
     const unsigned char* ks = st;
     const unsigned char* vs = st + C::KTILE;
-    const int key0 = (t0 + j) * BC;
+    const int key0 = tile_of(j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;     // every key follows every row of the wave
     if (MASK && W >= 0 && key0 + BC - 1 < q0 - W) return;   // below every row's window
-    if (bs && !bm_row[key0 >> 7]) return;   // block off
     const bool need_mask = (key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0) ||
                            (MASK && W >= 0 && key0 < q0 + 31 - W);
     const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
@@ -549,7 +589,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  issue(0, stage0);
+  if (n_tiles > 0) issue(0, stage0);   // (a block-sparse list can be empty)
   for (int j = 0; j < n_tiles; j += 2) {
     wait_vmem();
     __syncthreads();

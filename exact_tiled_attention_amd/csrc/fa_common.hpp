@@ -239,6 +239,40 @@ __device__ __forceinline__ PersistentMap persistent_map(int block, int workers, 
   }
   return m;
 }
+// Block-sparse attention (128 x 128 blocks, mask [H][nb][nb] of bytes): a
+// workgroup runs its tile loop over a list of only the key tiles that some
+// of its rows need, so a tile whose key block is off for all of them costs
+// nothing (no load, no step, no barrier).  Wave 0 reads query blocks
+// qb .. qb + ROWS - 1 of head h and writes, in key order, 4 t + f for each
+// key tile t (BC keys) in [t_first, t_first + n_all) with f != 0, bit r of
+// f set when query block qb + r has t's key block on; every wave of the
+// workgroup gets the count.  kMaxTiles bounds the list (N <= 131072 with
+// 64-key tiles).
+constexpr int kMaxTiles = 2048;
+template <int BC, int ROWS>
+__device__ __forceinline__ int list_tiles(const unsigned char* block_mask, int nb, int h, int qb, int t_first,
+                                          int n_all, unsigned short* list, int* count) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned char* row = block_mask + ((size_t)h * nb + qb) * nb;
+    int n = 0;
+    for (int base = 0; base < n_all; base += 64) {   // uniform trip count: every lane votes
+      const int t = t_first + base + lane;
+      int f = 0;
+      if (base + lane < n_all) {
+        const int kb = (t * BC) >> 7;
+        f = row[kb] != 0;
+        if (ROWS == 2 && qb + 1 < nb) f |= (row[nb + kb] != 0) << 1;
+      }
+      const unsigned long long bal = __ballot(f != 0);
+      if (f) list[n + __popcll(bal & ((1ull << lane) - 1))] = (unsigned short)(4 * t + f);
+      n += __popcll(bal);
+    }
+    if (lane == 0) *count = n;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*count);
+}
 // Item of round r for this worker, or -1 when its share is done.
 __device__ __forceinline__ int persistent_item(const PersistentMap& m, int r) {
   const int j = r * m.L + ((r & 1) ? m.L - 1 - m.c : m.c);

@@ -85,17 +85,6 @@ __device__ __forceinline__ ItemMask mask_of(const FwdParams& p, int b, int q_fir
   }
   return m;
 }
-// Block-sparse: a workgroup copies its query blocks' rows of the block mask
-// to LDS once per item (every tile then tests a byte there instead of
-// waiting on a global load); kMaxNb bounds a row (N <= 131072).
-constexpr int kMaxNb = 1024;
-__device__ __forceinline__ void stage_mask_rows(const FwdParams& p, int h, int qb, int rows,
-                                                unsigned char* dst) {
-  for (int i = threadIdx.x; i < rows * p.nb; i += blockDim.x) {
-    const int r = i / p.nb, kb = i - r * p.nb;
-    dst[r * kMaxNb + kb] = qb + r < p.nb ? p.block_mask[((size_t)h * p.nb + qb + r) * p.nb + kb] : 0;
-  }
-}
 // O = 0 (bf16) and LSE = -inf for a padding row, or a row that sees no key;
 // lanes l and l ^ 32 each write half of the row.
 __device__ __forceinline__ void write_empty_rows(const FwdParams& p, int bh, int myq, int g, int d) {
@@ -446,16 +435,17 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   }
   const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
   const int t0 = mk.t_begin;            // tiles j = 0.. stand for t0 + j
-  const int n_tiles = (kv_end + BC - 1) / BC - t0;
+  int n_tiles = (kv_end + BC - 1) / BC - t0;
   // Block-sparse: the workgroup's rows are one 128-row query block
-  // (BR = 128); tiles whose key block is off are neither loaded nor used.
+  // (BR = 128); step j takes the j-th tile of the list of tiles that are on.
   static_assert(!MASK || BR == 128, "block masks assume one query block per workgroup");
   const bool bs = MASK && p.block_mask;
-  __shared__ unsigned char bm_row[MASK ? kMaxNb : 1];
-  if (bs) {
-    stage_mask_rows(p, h, q_first >> 7, 1, bm_row);
-    __syncthreads();
-  }
+  __shared__ unsigned short tlist[MASK ? kMaxTiles : 1];
+  __shared__ int tcount;
+  if (bs) n_tiles = list_tiles<BC, 1>(p.block_mask, p.nb, h, q_first >> 7, t0, n_tiles, tlist, &tcount);
+  auto tile_of = [&](int j) -> int {
+    return bs ? __builtin_amdgcn_readfirstlane((int)tlist[j]) >> 2 : t0 + j;
+  };
 
   // Q operand (B of S^T = K Q^T): slot (kb, g, e) <-> column kb*16 + 8g + e.
   bf16x8 qr[D / 16];
@@ -495,9 +485,7 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
   float m_run = -INFINITY, l_run = 0.f;
 
   auto issue = [&](int j, unsigned char* st) {
-    const int key0 = (t0 + j) * BC;
-    // (with two stages every wait is for all loads, so a tile can be left out)
-    if (NST == 2 && bs && !bm_row[key0 >> 7]) return;
+    const int key0 = tile_of(j) * BC;
     const int bytes = min(L - key0, BC) * RB;   // rows past the end read as zero
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
@@ -510,10 +498,9 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
 
   auto consume = [&](int j, const unsigned char* kl) {
     const unsigned char* vl = kl + C::TILE;
-    const int key0 = (t0 + j) * BC;
+    const int key0 = tile_of(j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;   // every key of the tile follows every row of the wave
     if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return;   // below every row's window
-    if (bs && !bm_row[key0 >> 7]) return;                                     // block off
     f32x16 s[BC / 32];
 #pragma unroll
     for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
@@ -705,7 +692,8 @@ struct PpCfg {
 
 // One work item (head, 256-row query tile) of the ping-pong kernel.  With
 // MASK, sequence b is valid for its first len_b rows (p.seqlens) and, with a
-// window w >= 0, query i sees only keys i - w .. i (see mask_of).
+// window w >= 0, query i sees only keys i - w .. i (see mask_of).  (Block
+// masks go to the four-wave kernel, whose workgroup is one query block.)
 template <int D, bool CAUSAL, int BC_, bool LATE, bool MASK>
 __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   using C = PpCfg<D, BC_, LATE>;
@@ -739,17 +727,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   const int kv_end = CAUSAL ? min(L, q_first + BR) : L;
   const int t0 = mk.t_begin;            // first key tile any row of the item sees
   const int n_tiles = (kv_end + BC - 1) / BC - t0;   // tiles j = 0.. stand for t0 + j
-  // Block-sparse: the item's two 128-row query blocks (waves 0-3 and 4-7).
-  const bool bs = MASK && p.block_mask;
-  __shared__ unsigned char bm_rows[MASK ? 2 * kMaxNb : 1];
-  if (bs) {
-    stage_mask_rows(p, h, q_first >> 7, 2, bm_rows);
-    __syncthreads();
-  }
-  const unsigned char* bm_wave = bm_rows + (wid >> 2) * kMaxNb;
-  auto tile_needed = [&](int key0) -> bool {   // by some wave of the item
-    return (bm_rows[key0 >> 7] | bm_rows[kMaxNb + (key0 >> 7)]) != 0;
-  };
+  auto tile_of = [&](int j) -> int { return t0 + j; };
 
   bf16x8 qr[D / 16];
 #pragma unroll
@@ -788,10 +766,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   bf16x8 pk[NKB][2];
 
   auto issue_one = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
-    const int key0 = (t0 + j) * BC;
-    // (a tile no wave needs is not loaded; the LATE pipeline counts its loads,
-    // so there every tile is loaded)
-    if (!LATE && bs && !tile_needed(key0)) return;
+    const int key0 = tile_of(j) * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(L - key0, BC) * RB);
 #pragma unroll
     for (int i = 0; i < IPD; ++i) dma16_buf<0>(r, off[i], st + (dwid * IPD + i) * 1024);
@@ -800,10 +775,9 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   // the online softmax of S_j into P_j (packed bf16).
   f32x16 s[NKB];
   auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {
-    const int key0 = (t0 + j) * BC;
+    const int key0 = tile_of(j) * BC;
     if (CAUSAL && key0 > q0 + 31) return false;
     if (MASK && mk.window >= 0 && key0 + BC - 1 < q0 - mk.window) return false;   // below every row's window
-    if (bs && !bm_wave[key0 >> 7]) return false;                                  // block off for this wave
     // consecutive MFMAs go to different accumulators (no back-to-back chain)
 #pragma unroll
     for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
@@ -827,7 +801,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
     return true;
   };
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int key0 = (t0 + j) * BC;
+    const int key0 = tile_of(j) * BC;
     if ((key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0)) {
       // key = key0 + 4g + rel, rel a compile-time constant per register
       const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
@@ -1649,11 +1623,20 @@ static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
 //  * d = 64 causal: four independent waves per workgroup with 128-row tiles
 //    (twice the workgroups of the ping-pong kernel: better balance for short
 //    causal grids);
-//  * d = 256: wave pairs splitting the columns of O (two waves a SIMD).
+//  * d = 256: wave pairs splitting the columns of O (two waves a SIMD);
+//  * block-sparse: four independent waves with 128-row tiles, one query
+//    block per workgroup, so every step of its tile list is work for every
+//    wave (the ping-pong kernel's two query blocks often need different
+//    tiles; S1 forward 950 vs 784 TFLOP/s).
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
-    case 64: return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128, true>(p, s);
-    case 128: return causal ? launch_pp<128, true, 64, false>(p, s) : launch_pp<128, false, 64, false>(p, s);
+    case 64:
+      if (p.block_mask && !causal) return launch_bf16<64, false, 4, 64, FA_NST64>(p, s);
+      return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128, true>(p, s);
+    case 128:
+      if (p.block_mask)
+        return causal ? launch_bf16<128, true, 4, 64, 2>(p, s) : launch_bf16<128, false, 4, 64, 2>(p, s);
+      return causal ? launch_pp<128, true, 64, false>(p, s) : launch_pp<128, false, 64, false>(p, s);
 #if FA_D256_PAIRS
     case 256: return causal ? launch_pairs<256, true>(p, s) : launch_pairs<256, false>(p, s);
 #else
