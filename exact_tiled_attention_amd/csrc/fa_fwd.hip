@@ -55,6 +55,9 @@
 #ifndef FA_SUM_F32
 #define FA_SUM_F32 1
 #endif
+#ifndef SP_VALU_PER_MFMA
+#define SP_VALU_PER_MFMA 8
+#endif
 #ifndef FA_PERSIST
 #define FA_PERSIST 1
 #endif
@@ -661,6 +664,224 @@ void fwd_bf16_kernel(FwdParams p) {
   } else {
     fwd_bf16_kernel_item<D, CAUSAL, NW, BC_, NST, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
   }
+}
+
+// ============================================ bf16, software-pipelined ====
+// Four independent waves of 32 rows (128 per workgroup), as above, but each
+// wave overlaps its own work: the MFMAs of S_{j+1} = K_{j+1} Q^T are issued
+// among the exponentials of tile j (they do not depend on each other, so the
+// matrix pipe runs under the VALU), then P_j V_j follows.  A wave alone on
+// its SIMD (the last, longest items of a short causal grid) no longer leaves
+// one pipe idle while the other works.  K and V have stages of their own:
+// in step j the wave reads K_{j+1} and V_j while K_{j+2} and V_{j+1} load.
+// No tile is skipped for a wave (a tile past the wave's rows is masked out
+// instead), so every step has the same shape.  Every row sees a key of its
+// first tile (no mask but the causal one), which the lazy max relies on.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkItem wi) {
+  using C = Bf16Cfg<D, 4, 64, 2>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, NKB = BC / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * RB;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  auto key_of = [&](int j) -> int { return j * BC; };
+
+  bf16x8 qr[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    bf16x8 x = {};
+    if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
+    qr[kb] = x;
+  }
+  int dma_k[IPW], dma_v[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = (wid * IPW + i) * 1024 + lane * 16;
+    const int row = byte / RB, pu = (byte % RB) / 16;
+    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
+    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
+  }
+  constexpr int NKO = D / 16 < 8 ? D / 16 : 8, NVO = D / 32 < 4 ? D / 32 : 4;
+  int koff[NKO];
+#pragma unroll
+  for (int kb = 0; kb < NKO; ++kb) koff[kb] = lr * RB + k_swz<RB>(lr, 2 * kb + g) * 16;
+  const int s16 = lane & 15, G = lane >> 4;
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
+  int voff[NVO];
+#pragma unroll
+  for (int db = 0; db < NVO; ++db)
+    voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  const float c = p.scale_log2;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto issue = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
+    const int key0 = key_of(j);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
+  };
+  auto qk = [&](const unsigned char* kl, f32x16* s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const bf16x8 a = *(const bf16x8*)(kl + kb32 * 32 * RB + (kb / NKO) * 256 + koff[kb % NKO]);
+        s[kb32] = mfma_bf16(a, qr[kb], s[kb32]);
+      }
+  };
+  // causal diagonal and ragged tail: scores of keys a row does not see -> -inf
+  auto mask_tile = [&](int j, f32x16* s) __attribute__((always_inline)) {
+    const int key0 = key_of(j);
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb32 * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb32][r] = -INFINITY;
+    }
+  };
+  // P = exp2(S c - m) rounded to bf16, and the row sum of the rounded values
+  auto expo = [&](const f32x16* s, float m, bf16x8 (*pk)[2]) __attribute__((always_inline)) -> float {
+    float t = 0.f;
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
+          const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
+          w4[w] = pack_bf16(e0, e1);
+#if FA_SUM_F32
+          t += e0 + e1;
+#else
+          t = add_bf16_pair(w4[w], t);
+#endif
+        }
+        pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+      }
+    return t;
+  };
+  auto pv = [&](const unsigned char* vl, bf16x8 (*pk)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+          const bf16x4 lo = lds_read_tr16(vr);
+          const bf16x4 hi = lds_read_tr16(vr + 8 * RB);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
+        }
+      }
+  };
+  // Step j: S_j is in scur; K_{j+1} and V_j were issued one step earlier.
+  auto step = [&](int j, f32x16* scur, f32x16* snext, const unsigned char* knext, const unsigned char* vcur,
+                  unsigned char* k_load, unsigned char* v_load) __attribute__((always_inline)) {
+    wait_vmem();
+    barrier_lds();   // K_{j+1}, V_j visible; the stages of K_j and V_{j-1} free
+    if (j + 1 < n_tiles) issue(vg, dma_v, j + 1, v_load);
+    if (j + 2 < n_tiles) issue(kg, dma_k, j + 2, k_load);
+    mask_tile(j, scur);
+    bf16x8 pk[NKB][2];
+    float ts;
+    if (j + 1 < n_tiles) {
+      qk(knext, snext);
+      ts = expo(scur, m_run, pk);
+      // the K reads lead; then each MFMA is followed by its share of the VALU
+      constexpr int NM = NKB * (D / 16);
+      constexpr int PF = QK_PREFETCH < NM ? QK_PREFETCH : NM;
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + PF < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, SP_VALU_PER_MFMA, 0);
+      }
+    } else {
+      ts = expo(scur, m_run, pk);
+    }
+    // the tile max only when some partial row sum leaves [0, kSumBound]
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb32][r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ts = expo(scur, m_run, pk);
+    }
+    l_run += ts;
+    pv(vcur, pk);
+  };
+
+  f32x16 sa[NKB], sb[NKB];
+  issue(kg, dma_k, 0, ks0);
+  issue(vg, dma_v, 0, vs0);
+  if (n_tiles > 1) issue(kg, dma_k, 1, ks1);
+  wait_vmem();
+  barrier_lds();
+  qk(ks0, sa);
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, sa, sb, ks1, vs0, ks0, vs1);
+    if (j + 1 < n_tiles) step(j + 1, sb, sa, ks0, vs1, ks1, vs0);
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_sp_kernel(FwdParams p) {
+  fwd_bf16_sp_item<D, CAUSAL>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
 }
 
 // =================================================== bf16, ping-pong =====
@@ -1593,6 +1814,15 @@ static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
 }
 
 template <int D, bool CAUSAL>
+static hipError_t launch_sp(FwdParams& p, hipStream_t s) {
+  // one workgroup per item (two resident per CU)
+  using C = Bf16Cfg<D, 4, 64, 2>;
+  finish_grid(p, C::BR);
+  hipLaunchKernelGGL((fwd_bf16_sp_kernel<D, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
   // Causal: as many workgroups as fit, each looping over its share of the
   // items (C2b 0.348 vs 0.378 ms with one workgroup per item, although the
@@ -1635,7 +1865,8 @@ static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
 //  * d = 64 non-causal: ping-pong, 128-key tiles, DMA at the end of a phase;
 //  * d = 64 causal: four independent waves per workgroup with 128-row tiles
 //    (twice the workgroups of the ping-pong kernel: better balance for short
-//    causal grids);
+//    causal grids), each wave software-pipelined when there is no other mask
+//    (C2a 0.103 vs 0.109 ms, C4 922 vs 893 TFLOP/s);
 //  * d = 256: wave pairs splitting the columns of O (two waves a SIMD);
 //  * block-sparse: four independent waves with 128-row tiles, one query
 //    block per workgroup, so every step of its tile list is work for every
@@ -1644,6 +1875,7 @@ static hipError_t launch_pp(FwdParams& p, hipStream_t s) {
 hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
     case 64:
+      if (causal && !masked(p)) return launch_sp<64, true>(p, s);
       if (p.block_mask && !causal) return launch_bf16<64, false, 4, 64, FA_NST64>(p, s);
       return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128, true>(p, s);
     case 128:
