@@ -160,13 +160,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     dv[i] = f32x16{};
   }
 
-  int dma_off[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int byte = (wid * IPW + i) * 1024 + lane * 16;
-    const int row = byte / RB, pu = (byte % RB) / 16;
-    dma_off[i] = row * RB + rt_swz<RB>(row, pu) * 16;
-  }
+  const int dma0 = dma_base<RB, kSwzRt>(wid * IPW, lane);
   int roff[D / 16];
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) roff[kb] = lr * RB + rt_swz<RB>(lr, 2 * kb + g) * 16;
@@ -235,8 +229,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const bf16*)p.dout + (bh * N + row0) * D, rows * RB);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      dma16_buf<0>(rq, dma_off[i], st + (wid * IPW + i) * 1024);
-      dma16_buf<0>(rd, dma_off[i], st + C::QTILE + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rq, dma_off<RB, kSwzRt>(dma0, i), st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rd, dma_off<RB, kSwzRt>(dma0, i), st + C::QTILE + (wid * IPW + i) * 1024);
     }
     if (wid < 2) {   // wave 0: LSE2 of the tile's rows, wave 1: D (padded rows read 0)
       const float* src = (wid == 0 ? p.lse2 : p.delta) + bh * N + row0;
@@ -436,13 +430,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
-  int dma_off[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int byte = (wid * IPW + i) * 1024 + lane * 16;
-    const int row = byte / RB, pu = (byte % RB) / 16;
-    dma_off[i] = row * RB + rt_swz<RB>(row, pu) * 16;
-  }
+  const int dma0 = dma_base<RB, kSwzRt>(wid * IPW, lane);
   int roff[D / 16];
 #pragma unroll
   for (int kb = 0; kb < D / 16; ++kb) roff[kb] = lr * RB + rt_swz<RB>(lr, 2 * kb + g) * 16;
@@ -473,8 +461,8 @@ void bwd_dq_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      dma16_buf<0>(rk, dma_off[i], st + (wid * IPW + i) * 1024);
-      dma16_buf<0>(rv, dma_off[i], st + C::KTILE + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rk, dma_off<RB, kSwzRt>(dma0, i), st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rv, dma_off<RB, kSwzRt>(dma0, i), st + C::KTILE + (wid * IPW + i) * 1024);
     }
   };
 

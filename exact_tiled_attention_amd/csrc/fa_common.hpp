@@ -172,6 +172,33 @@ __device__ __forceinline__ int v_swz(int row, int u) {
   return RB == 128 ? (u ^ (((row >> 1) & 1) << 2)) : (u ^ (((row & 1) << 3) | ((row & 2) << 1)));
 }
 
+// Global byte offsets of a wave's 16-byte LDS-DMA copies of a tile of rows
+// of RB bytes stored row-swizzled (kind S: rt_swz, k_swz or v_swz).  The
+// wave copies KBs k0 .. k0 + n - 1 (n a power of two dividing k0); each
+// swizzle XORs row bits into unit bits, and the row bits that change with i
+// (i * 1024 / RB) never overlap those from the lane or from k0, so copy i is
+// at copy 0's offset XOR a constant, plus i KB: one register serves all of
+// the wave's copies.  (The empty asm hides the base's value, so the compiler
+// forms each offset where it is used instead of keeping all of them live.)
+enum { kSwzRt = 0, kSwzK = 1, kSwzV = 2 };
+template <int RB, int S>
+__device__ __forceinline__ int swz_of(int row, int u) {
+  if constexpr (S == kSwzRt) return rt_swz<RB>(row, u);
+  else if constexpr (S == kSwzK) return k_swz<RB>(row, u);
+  else return v_swz<RB>(row, u);
+}
+template <int RB, int S>
+__device__ __forceinline__ int dma_base(int k0, int lane) {
+  const int byte = k0 * 1024 + lane * 16;
+  const int row = byte / RB, pu = (byte % RB) / 16;
+  return row * RB + swz_of<RB, S>(row, pu) * 16;
+}
+template <int RB, int S>
+__device__ __forceinline__ int dma_off(int base, int i) {
+  asm volatile("" : "+v"(base));
+  return (base ^ (swz_of<RB, S>(i * (1024 / RB), 0) * 16)) + i * 1024;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -1302,14 +1302,8 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
     if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
     qr[kb] = x;
   }
-  int dma_k[IPW], dma_v[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int byte = (wid * IPW + i) * 1024 + lane * 16;
-    const int row = byte / RB, pu = (byte % RB) / 16;
-    dma_k[i] = row * RB + k_swz<RB>(row, pu) * 16;
-    dma_v[i] = row * RB + v_swz<RB>(row, pu) * 16;
-  }
+  const int dma_k0 = dma_base<RB, kSwzK>(wid * IPW, lane);
+  const int dma_v0 = dma_base<RB, kSwzV>(wid * IPW, lane);
   // The swizzles touch only the low 4 bits of a 16-byte unit index, so units
   // 16 apart share one per-lane offset (+256 bytes, an immediate).
   constexpr int NKO = 8, NVO = DH / 32;
@@ -1337,11 +1331,13 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   float* mb = mbuf + pr * 64 + lane;
   float* sb = sbuf + pr * 64 + lane;
 
-  auto issue = [&](const unsigned char* src, const int* off, int t, unsigned char* st) {
+  auto issue = [&](const unsigned char* src, bool is_k, int t, unsigned char* st) {
     const int key0 = (t0 + t) * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(L - key0, BC) * RB);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
+    for (int i = 0; i < IPW; ++i)
+      dma16_buf<0>(r, is_k ? dma_off<RB, kSwzK>(dma_k0, i) : dma_off<RB, kSwzV>(dma_v0, i),
+                   st + (wid * IPW + i) * 1024);
   };
   auto qk = [&](const unsigned char* kl) {
 #pragma unroll
@@ -1473,8 +1469,8 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
   auto begin = [&](int ph, unsigned char* k_load, unsigned char* v_load) {
     wait_vmem();
     __syncthreads();
-    if (ph + 2 < n_tiles) issue(kg, dma_k, ph + 2, k_load);
-    if (ph >= 0 && ph < n_tiles) issue(vg, dma_v, ph, v_load);
+    if (ph + 2 < n_tiles) issue(kg, true, ph + 2, k_load);
+    if (ph >= 0 && ph < n_tiles) issue(vg, false, ph, v_load);
   };
   auto as_owner = [&](int ph, const unsigned char* v_use) {
     // the partner's tile ph - 1: its max, row sums and P come from LDS
@@ -1493,7 +1489,7 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
     if (ph + 1 >= t_beg && ph + 1 < t_end) qk(k_use);
   };
 
-  issue(kg, dma_k, 0, k0);
+  issue(kg, true, 0, k0);
   if (role == 0) {
     for (int ph = -1; ph <= n_tiles; ph += 2) {
       begin(ph, k1, v1);                  // ph odd: K_{ph+1} in k0, V_{ph-1} in v0
@@ -1825,9 +1821,8 @@ static hipError_t launch_sp(FwdParams& p, hipStream_t s) {
 template <int D, bool CAUSAL>
 static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
   // Causal: as many workgroups as fit, each looping over its share of the
-  // items (C2b 0.348 vs 0.378 ms with one workgroup per item, although the
-  // looping instance spills two registers); non-causal: one workgroup per
-  // item (the looping grid measured 1.5% slower).
+  // items (C2b 0.348 vs 0.378 ms with one workgroup per item); non-causal:
+  // one workgroup per item (the looping grid measured 1.5% slower).
   finish_grid(p, PairCfg<D>::BR);
   if constexpr (CAUSAL) {
     if (masked(p)) {
