@@ -56,11 +56,12 @@ template <bool MASK>
 __device__ __forceinline__ int valid_len(const BwdParams& p, int b) {
   return MASK && p.seqlens ? min(max(p.seqlens[b], 0), p.N) : p.N;
 }
-// Block-sparse: the dK/dV kernel keeps its key block's column of the mask
-// over a GQA group in LDS as bits ((H / H_kv) * nb <= kMaxMaskBits: 2 KB,
-// so its occupancy is unchanged) and steps from one set bit's query tiles
-// to the next; the dQ kernel runs over a list of its key tiles that are on.
-constexpr int kMaxMaskBits = 16384;
+// Block-sparse: the dK/dV kernel keeps, in LDS, one bit per step (query tile
+// and GQA head) of its key block's column of the mask (H / H_kv) * 2 nb <=
+// kMaxMaskBits: 4 KB, so its occupancy is unchanged) and steps from one
+// set bit to the next; the dQ kernel runs over a list of its key tiles that
+// are on.
+constexpr int kMaxMaskBits = 32768;
 // A 64-bit LDS word every lane of the wave reads at one address, made
 // scalar (so loops over it stay uniform).
 __device__ __forceinline__ unsigned long long lds_u64_uniform(const unsigned long long* a) {
@@ -177,24 +178,33 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int per_head = max(0, qt_stop - qt_start);
   const int n_iter = G * per_head;
   const float c = p.scale_log2;
+  // Step it takes query tile qt_stop - 1 - it / G of group head it % G: the
+  // latest query tiles first, the group's heads innermost.  So all running
+  // workgroups of one (batch, K/V head) read the same Q and dO tile at the
+  // same time, and each tile comes from HBM once and from L2 after that
+  // (taking each head's tiles upward from the diagonal instead spread them
+  // over many tiles at once: 6x the compulsory reads on the GQA prefill
+  // shape, against 1x for the dQ kernel).
+  auto step_tile = [&](int it, int& gi, int& qt) {
+    const int qi = it / G;
+    gi = it - qi * G;
+    qt = qt_stop - 1 - qi;
+  };
 
-  // Block-sparse: the key block is one 128-key block (BKV = 128).  Bit
-  // gi * nb + qb is set when query block qb of group head gi has it on and
-  // holds some of the tiles [qt_start, qt_stop); steps in the order of
-  // it_idx (gi major) then visit only the tiles of set bits.
+  // Block-sparse: the key block is one 128-key block (BKV = 128).  Bit it
+  // is set when step it's tile is in a query block that has the key block
+  // on for its head, and steps visit only the set bits.
   static_assert(!MASK || BKV == 128, "block masks assume one key block per workgroup");
-  static_assert(128 % BQ == 0, "query tiles split a mask block");
   const bool bs = MASK && p.block_mask;
   __shared__ unsigned long long bm_col[MASK ? kMaxMaskBits / 64 : 1];
-  const int n_bits = G * p.nb;
   if (bs) {
-    for (int base = 0; base < n_bits; base += 256) {   // uniform trip count: every lane votes
+    for (int base = 0; base < n_iter; base += 256) {   // uniform trip count: every lane votes
       const int i = base + tid;
       bool on = false;
-      if (i < n_bits) {
-        const int gi = i / p.nb, qb = i - gi * p.nb;
-        on = qb * (128 / BQ) < qt_stop && (qb + 1) * (128 / BQ) > qt_start &&
-             p.block_mask[((size_t)(kvh * G + gi) * p.nb + qb) * p.nb + (k_first >> 7)] != 0;
+      if (i < n_iter) {
+        int gi, qt;
+        step_tile(i, gi, qt);
+        on = p.block_mask[((size_t)(kvh * G + gi) * p.nb + ((qt * BQ) >> 7)) * p.nb + (k_first >> 7)] != 0;
       }
       const unsigned long long bits = __ballot(on);
       if ((tid & 63) == 0) bm_col[(base + tid) >> 6] = bits;
@@ -204,24 +214,17 @@ void bwd_dkdv_kernel(BwdParams p) {
   // first step >= it whose tile is on (n_iter if none)
   auto next_on = [&](int it) -> int {
     if (!bs || it >= n_iter) return it;
-    const int gi = it / per_head;
-    const int qt = qt_start + (it - gi * per_head);
-    const int bit = gi * p.nb + ((qt * BQ) >> 7);
-    int word = bit >> 6;
-    unsigned long long w = lds_u64_uniform(bm_col + word);
-    if ((w >> (bit & 63)) & 1ull) return it;
-    w &= (~0ull << (bit & 63)) << 1;                     // the bits after this block's
+    int word = it >> 6;
+    unsigned long long w = lds_u64_uniform(bm_col + word) & (~0ull << (it & 63));
     while (w == 0) {
-      if (++word >= (n_bits + 63) >> 6) return n_iter;
+      if (++word >= (n_iter + 63) >> 6) return n_iter;
       w = lds_u64_uniform(bm_col + word);
     }
-    const int nbit = word * 64 + __builtin_ctzll(w);
-    const int gi2 = nbit / p.nb, qb2 = nbit - gi2 * p.nb;
-    return gi2 * per_head + max(qb2 * (128 / BQ), qt_start) - qt_start;
+    return word * 64 + __builtin_ctzll(w);
   };
   auto issue = [&](int it_idx, unsigned char* st) {
-    const int gi = it_idx / per_head;
-    const int qt = qt_start + (it_idx - gi * per_head);
+    int gi, qt;
+    step_tile(it_idx, gi, qt);
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
     const int row0 = qt * BQ;
     const int rows = min(L - row0, BQ);          // rows past the valid ones read as zero
@@ -240,8 +243,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
 
   auto consume = [&](int it_idx, const unsigned char* st) {
-    const int gi = it_idx / per_head;
-    const int qrow0 = (qt_start + (it_idx - gi * per_head)) * BQ;
+    int gi, qt;
+    step_tile(it_idx, gi, qt);
+    const int qrow0 = qt * BQ;
     const unsigned char* qs = st;
     const unsigned char* ds = st + C::QTILE;
     const float* lse2 = (const float*)(st + 2 * C::QTILE);
