@@ -102,10 +102,9 @@ struct DkdvCfg {
   static_assert(IPW >= 1, "tile too small for the DMA split");
 };
 
-// d = 128 keeps K, V, dK and dV of 32 keys in registers (192 a lane); at two
-// waves a SIMD a few values spill to scratch.  Measured on MI355X, that is
-// still faster than one wave a SIMD without spills (710 vs 649 TFLOP/s causal
-// at B=2, H=16, N=8192), so the instance keeps two waves.
+// d = 128 keeps K, V, dK and dV of 32 keys in registers (192 a lane) at two
+// waves a SIMD (faster than one wave a SIMD: 710 vs 649 TFLOP/s causal at
+// B=2, H=16, N=8192); the causal and masked instances still spill two values.
 // With MASK (padding mask and/or sliding window, as in the forward) a key
 // block sees only the query tiles whose rows are valid and whose windows
 // reach it, and keys past the valid length get zero gradients.
@@ -162,14 +161,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 
   const int dma0 = dma_base<RB, kSwzRt>(wid * IPW, lane);
-  int roff[D / 16];
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) roff[kb] = lr * RB + rt_swz<RB>(lr, 2 * kb + g) * 16;
-  int troff[2][D / 32];
-#pragma unroll
-  for (int sec = 0; sec < 2; ++sec)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) troff[sec][db] = tr_off<RB>(lane, sec, db);
+  // LDS read offsets of block 0 (the others are formed per tile, below)
+  const int roff0 = lr * RB + rt_swz<RB>(lr, g) * 16;
+  const int troff0 = tr_off<RB>(lane, 0, 0);
 
   const int n_qt = (L + BQ - 1) / BQ;        // tiles holding valid query rows
   const int qt_start = CAUSAL ? k_first / BQ : 0;
@@ -246,13 +240,23 @@ void bwd_dkdv_kernel(BwdParams p) {
     int gi, qt;
     step_tile(it_idx, gi, qt);
     const int qrow0 = qt * BQ;
+    // The read offsets from one register each: block kb's, or section sec
+    // and column block db's, are block 0's XOR a constant (the swizzle is
+    // XOR-linear in bits no lane bit shares, as for the DMA copies); made
+    // opaque once per tile so they are formed here instead of kept live.
+    int rb0 = roff0, tb0 = troff0;
+    asm volatile("" : "+v"(rb0), "+v"(tb0));
+    auto RO = [&](int kb) { return rb0 ^ (rt_swz<RB>(0, 2 * kb) * 16); };
+    auto TO = [&](int sec, int db) { return (tb0 ^ (rt_swz<RB>(8 * sec, db * 4) * 16)) + sec * 8 * RB; };
     const unsigned char* qs = st;
     const unsigned char* ds = st + C::QTILE;
     const float* lse2 = (const float*)(st + 2 * C::QTILE);
     const float* dl = lse2 + BQ;
-    // (at d = 256 the two 32-query halves run one after the other: unrolled,
-    // their temporaries would not fit next to K, V, dK and dV)
-#pragma unroll (D > 128 ? 1 : BQ / 32)
+    // (at d >= 128 the two 32-query halves run one after the other: unrolled,
+    // their temporaries do not fit next to K, V, dK and dV; at d = 128 that
+    // and the offsets formed per tile took the spills from 44 to 8 bytes and
+    // the GQA prefill backward from 565 to 632 TFLOP/s)
+#pragma unroll (D >= 128 ? 1 : BQ / 32)
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int qq0 = qrow0 + qb * 32;
       if (CAUSAL && qq0 + 31 < kw0) continue;   // every query precedes every key
@@ -261,8 +265,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 aq = *(const bf16x8*)(qs + qb * 32 * RB + roff[kb]);
-        const bf16x8 ad = *(const bf16x8*)(ds + qb * 32 * RB + roff[kb]);
+        const bf16x8 aq = *(const bf16x8*)(qs + qb * 32 * RB + RO(kb));
+        const bf16x8 ad = *(const bf16x8*)(ds + qb * 32 * RB + RO(kb));
         s = mfma_bf16(aq, kr[kb], s);
         dp = mfma_bf16(ad, vr[kb], dp);
       }
@@ -304,10 +308,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int rb = (qb * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 dlo = lds_read_tr16(ds + rb + troff[0][db]);
-          const bf16x4 dhi = lds_read_tr16(ds + rb + troff[1][db]);
-          const bf16x4 qlo = lds_read_tr16(qs + rb + troff[0][db]);
-          const bf16x4 qhi = lds_read_tr16(qs + rb + troff[1][db]);
+          const bf16x4 dlo = lds_read_tr16(ds + rb + TO(0, db));
+          const bf16x4 dhi = lds_read_tr16(ds + rb + TO(1, db));
+          const bf16x4 qlo = lds_read_tr16(qs + rb + TO(0, db));
+          const bf16x4 qhi = lds_read_tr16(qs + rb + TO(1, db));
           dv[db] = mfma_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
           dk[db] = mfma_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), sb, dk[db]);
         }
@@ -473,6 +477,8 @@ void bwd_dq_kernel(BwdParams p) {
   auto consume = [&](int j, const unsigned char* st) {
     const unsigned char* ks = st;
     const unsigned char* vs = st + C::KTILE;
+    auto RO = [&](int kb) { return roff[kb]; };
+    auto TO = [&](int sec, int db) { return troff[sec][db]; };
     const int key0 = tile_of(j) * BC;
     if (CAUSAL && key0 > q0 + 31) return;     // every key follows every row of the wave
     if (MASK && W >= 0 && key0 + BC - 1 < q0 - W) return;   // below every row's window
@@ -486,8 +492,8 @@ void bwd_dq_kernel(BwdParams p) {
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + roff[kb]);
-        const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + roff[kb]);
+        const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + RO(kb));
+        const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + RO(kb));
         s = mfma_bf16(ak, qr[kb], s);
         dp = mfma_bf16(av, dor[kb], dp);
       }
@@ -518,8 +524,8 @@ void bwd_dq_kernel(BwdParams p) {
         const int rb = (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo4 = lds_read_tr16(ks + rb + troff[0][db]);
-          const bf16x4 hi4 = lds_read_tr16(ks + rb + troff[1][db]);
+          const bf16x4 lo4 = lds_read_tr16(ks + rb + TO(0, db));
+          const bf16x4 hi4 = lds_read_tr16(ks + rb + TO(1, db));
           dq[db] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), ds2[half], dq[db]);
         }
       }
@@ -540,8 +546,8 @@ void bwd_dq_kernel(BwdParams p) {
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + roff[kb]);
-          const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + roff[kb]);
+          const bf16x8 ak = *(const bf16x8*)(ks + kb32 * 32 * RB + RO(kb));
+          const bf16x8 av = *(const bf16x8*)(vs + kb32 * 32 * RB + RO(kb));
           s = mfma_bf16(ak, qr[kb], s);
           dp = mfma_bf16(av, dor[kb], dp);
         }
@@ -573,8 +579,8 @@ void bwd_dq_kernel(BwdParams p) {
           const int rb = (kb32 * 32 + 16 * half) * RB;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x4 lo4 = lds_read_tr16(ks + rb + troff[0][db]);
-            const bf16x4 hi4 = lds_read_tr16(ks + rb + troff[1][db]);
+            const bf16x4 lo4 = lds_read_tr16(ks + rb + TO(0, db));
+            const bf16x4 hi4 = lds_read_tr16(ks + rb + TO(1, db));
             dq[db] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kb32][half], dq[db]);
           }
         }
