@@ -51,21 +51,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[1] = (bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
-  bf16x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (bf16)p[i];
-  return v;
-}
-// Two bf16 halves taken from the low (sel=0) or high (sel=1) 16 bits of a and b.
-__device__ __forceinline__ uint32_t perm_lo16(uint32_t a, uint32_t b) {
-  // result = (b.lo16 << 16) | a.lo16
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t perm_hi16(uint32_t a, uint32_t b) {
-  // result = (b.hi16 << 16) | a.hi16
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
 
 // ---------------------------------------------------------- exchanges -----
 // Combine a value across lane l and lane l^32 (the two halves of a wave hold

@@ -13,20 +13,20 @@
 // S^T = K Q^T, so that in the MFMA output layout one lane holds one query
 // row (16 keys per 32-key block, the other 16 in lane l^32): the row max and
 // row sum need one cross-half exchange instead of a 32-lane reduction.  The
-// probabilities then feed O^T += V^T P^T directly as the B operand, with V
-// staged transposed in LDS.
+// probabilities then feed O^T += V^T P^T directly as the B operand, with the
+// V^T fragments taken from row-major V tiles by the transposing LDS read.
 //
 // Online softmax ("FlashAttentionとは？…", 最大値と正規化項を持ち回るオンライン
 // softmaxの再スケール): running max m and running sum l per row; exp2 with
 // scale*log2(e) folded into one FMA; 1/l applied once in the epilogue.  The
 // result is exact up to rounding for any m, as long as numerator and
 // denominator use the same one and exp2(score - m) stays in range, so m is
-// moved (and the accumulator rescaled) only when needed.  The fp8 and fp32
-// kernels take each tile's max and move m when it exceeds m by more than
-// kRescaleSlack; the bf16 kernels do not even take the max: they form P
-// against the current m and fall back to the max-and-rescale path only when
-// a lane's partial row sum leaves [0, kSumBound] (a wave-uniform test that
-// also catches the first tile, where m is still -inf).
+// moved (and the accumulator rescaled) only when needed.  The fp32 kernel
+// takes each tile's max and moves m when it exceeds m by more than
+// kRescaleSlack; the bf16 and fp8 kernels do not even take the max: they
+// form P against the current m and fall back to the max-and-rescale path
+// only when a lane's partial row sum leaves [0, kSumBound] (a wave-uniform
+// test that also catches the first tile, where m is still -inf).
 //
 // Causal: key tiles past the work-group's last query are never loaded; the
 // mask is applied only on tiles that straddle the diagonal or the sequence
@@ -95,300 +95,6 @@ __device__ __forceinline__ void write_empty_rows(const FwdParams& p, int bh, int
   bf16* orow = (bf16*)p.o + ((size_t)bh * p.N + myq) * d;
   for (int c = 4 * g; c < d; c += 8) *(i32x2*)(orow + c) = i32x2{0, 0};
   if (p.lse && g == 0) p.lse[(size_t)bh * p.N + myq] = -INFINITY;
-}
-
-// ===================================================== bf16 / fp8 ========
-template <int D, bool CAUSAL, bool FP8>
-struct FwdCfg {
-  static constexpr int NW = 4;              // waves per workgroup
-  static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * 32;        // query rows per workgroup
-  static constexpr int BC = 64;             // keys per tile
-  static constexpr int QE = FP8 ? 1 : 2;    // bytes per Q/K/V element
-  static constexpr int KSB = D * QE + 16;   // K row stride in LDS (bytes)
-  static constexpr int VS = BC + 4;         // V^T row stride in LDS (bf16 elements)
-  static constexpr int KBUF = BC * KSB;     // bytes
-  static constexpr int VBUF = D * VS * 2;   // bytes
-  static constexpr int BUF = KBUF + VBUF;
-  static constexpr int CPR = D * QE / 16;   // 16-byte chunks per K/V row
-  static constexpr int KCH = BC * CPR / NT; // K chunks per thread
-  static constexpr int VE = 16 / QE;        // elements per 16-byte V chunk
-  static constexpr int NVB = (BC / 4) * (D / VE);   // V blocks of 4 keys x VE cols
-  static constexpr int VBT = (NVB + NT - 1) / NT;   // V blocks per thread
-  static_assert(BC * CPR % NT == 0, "K tile must split evenly");
-};
-
-template <int D, bool CAUSAL, bool FP8>
-__device__ __forceinline__ void fwd_mfma_kernel_item(const FwdParams& p, const WorkItem wi) {
-  // Two waves per SIMD (<= 256 registers each) let one wave's softmax VALU
-  // work overlap the other wave's MFMAs; d = 256 cannot fit and runs at one.
-  using C = FwdCfg<D, CAUSAL, FP8>;
-  constexpr int BR = C::BR, BC = C::BC, NT = C::NT;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF];
-
-  const int tid = threadIdx.x;
-  const int wid = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const int N = p.N;
-  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
-  const int kvh = h / (p.H / p.H_kv);
-  const int bkv = b * p.H_kv + kvh;
-  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * D * C::QE;
-  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * D * C::QE;
-  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * D * C::QE;
-
-  const int q_first = wi.qt * BR;
-  const int q0 = q_first + wid * 32;        // this wave's first query
-  const int myq = q0 + lr;                  // this lane's query row
-  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-
-  // ---- Q operand (B of S^T = K Q^T), resident in registers -----------------
-  // bf16: slot (kb, g, e) <-> column kb*16 + 8g + e; fp8: kb*64 + 32g + e.
-  constexpr int QREGS = FP8 ? D / 64 : D / 16;
-  typedef typename std::conditional<FP8, i32x8, bf16x8>::type qop_t;
-  qop_t qr[QREGS];
-#pragma unroll
-  for (int kb = 0; kb < QREGS; ++kb) {
-    if constexpr (FP8) {
-      i32x8 x = {};
-      if (myq < N) {
-        const i32x4* src = (const i32x4*)(qg + (size_t)myq * D + kb * 64 + 32 * g);
-        i32x4 lo = src[0], hi = src[1];
-        x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      qr[kb] = x;
-    } else {
-      bf16x8 x = {};
-      if (myq < N) x = *(const bf16x8*)(qg + ((size_t)myq * D + kb * 16 + 8 * g) * 2);
-      qr[kb] = x;
-    }
-  }
-
-  float c_base = p.scale_log2;
-  if constexpr (FP8) c_base *= p.qs[(size_t)wi.bh * ((N + 127) >> 7) + (q_first >> 7)];
-  const float* ksc = FP8 ? p.ks + (size_t)bkv * ((N + 127) >> 7) : nullptr;
-  const float* vsc = FP8 ? p.vs + (size_t)bkv * ((N + 127) >> 7) : nullptr;
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  // ---- tile staging: global -> registers -> LDS ----------------------------
-  i32x4 kreg[C::KCH];
-  i32x4 vreg[C::VBT][4];
-  auto load_tile = [&](int j) {
-    const int key0 = j * BC;
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int c = tid + it * NT;
-      const int row = c / C::CPR, col = c - row * C::CPR;
-      const int key = key0 + row;
-      i32x4 x = {};
-      if (key < N) x = *(const i32x4*)(kg + ((size_t)key * D * C::QE + col * 16));
-      kreg[it] = x;
-    }
-#pragma unroll
-    for (int it = 0; it < C::VBT; ++it) {
-      const int blk = tid + it * NT;
-      const int kq = blk % (BC / 4), cc = blk / (BC / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + kq * 4 + r;
-        i32x4 x = {};
-        if (blk < C::NVB && key < N) x = *(const i32x4*)(vg + ((size_t)key * D * C::QE + cc * 16));
-        vreg[it][r] = x;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kl = smem + buf * C::BUF;
-    bf16* vt = (bf16*)(kl + C::KBUF);
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int c = tid + it * NT;
-      const int row = c / C::CPR, col = c - row * C::CPR;
-      *(i32x4*)(kl + row * C::KSB + col * 16) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VBT; ++it) {
-      const int blk = tid + it * NT;
-      if (blk < C::NVB) {
-        const int kq = blk % (BC / 4), cc = blk / (BC / 4);
-        if constexpr (FP8) {
-          // 16 fp8 columns per chunk -> bf16 (exact: e4m3 has 3 fraction bits)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-#pragma unroll
-            for (int hw = 0; hw < 2; ++hw) {
-              float f[4][2];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                auto t = hw ? __builtin_amdgcn_cvt_pk_f32_fp8(vreg[it][r][w], true)
-                            : __builtin_amdgcn_cvt_pk_f32_fp8(vreg[it][r][w], false);
-                f[r][0] = t[0];
-                f[r][1] = t[1];
-              }
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                const int col = cc * 16 + w * 4 + hw * 2 + e;
-                uint32_t lo = pack_bf16(f[0][e], f[1][e]);
-                uint32_t hi = pack_bf16(f[2][e], f[3][e]);
-                *(i32x2*)(vt + col * C::VS + kq * 4) = i32x2{(int)lo, (int)hi};
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t a0 = vreg[it][0][w], a1 = vreg[it][1][w];
-            const uint32_t a2 = vreg[it][2][w], a3 = vreg[it][3][w];
-            const int col = cc * 8 + w * 2;
-            *(i32x2*)(vt + col * C::VS + kq * 4) =
-                i32x2{(int)perm_lo16(a0, a1), (int)perm_lo16(a2, a3)};
-            *(i32x2*)(vt + (col + 1) * C::VS + kq * 4) =
-                i32x2{(int)perm_hi16(a0, a1), (int)perm_hi16(a2, a3)};
-          }
-        }
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-
-  for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
-    const int key0 = j * BC;
-    // Waves whose rows all precede this tile see none of its keys.
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      const unsigned char* kl = smem + (j & 1) * C::BUF;
-      const bf16* vt = (const bf16*)(kl + C::KBUF);
-      // ---- S^T = K Q^T ------------------------------------------------------
-      f32x16 s[BC / 32];
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32) {
-        f32x16 acc = {};
-        const unsigned char* krow = kl + (kb32 * 32 + lr) * C::KSB;
-#pragma unroll
-        for (int kb = 0; kb < QREGS; ++kb) {
-          if constexpr (FP8) {
-            const i32x4* src = (const i32x4*)(krow + kb * 64 + 32 * g);
-            i32x4 lo = src[0], hi = src[1];
-            i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc = mfma_fp8(a, qr[kb], acc);
-          } else {
-            bf16x8 a = *(const bf16x8*)(krow + (kb * 16 + 8 * g) * 2);
-            acc = mfma_bf16(a, qr[kb], acc);
-          }
-        }
-        s[kb32] = acc;
-      }
-      // ---- mask (diagonal / tail tiles only) -------------------------------
-      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb32 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > myq) || key >= N) s[kb32][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax ----------------------------------------------------
-      float c = c_base;
-      if constexpr (FP8) c *= ksc[key0 >> 7];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
-      mx = max_halves(mx);
-      const float m_cand = mx * c;
-      if (__any(m_cand > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, m_cand);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
-      float madj = m_run;
-      float inv_sv = 1.f;
-      if constexpr (FP8) {
-        const float sv = vsc[key0 >> 7];
-        madj -= fast_log2(sv);   // p' = p * sV folds V's block scale into P
-        inv_sv = 1.f / sv;
-      }
-      float ts = 0.f;
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kb32][r], c, -madj));
-          s[kb32][r] = e;
-          ts += e;
-        }
-      l_run += FP8 ? ts * inv_sv : ts;
-      // ---- O^T += V^T P^T ----------------------------------------------------
-#pragma unroll
-      for (int kb32 = 0; kb32 < BC / 32; ++kb32)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = s[kb32][half * 8 + e];
-          const bf16x8 pb = pack_bf16x8(pv);
-          const int kcol = kb32 * 32 + 16 * half + 4 * g;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const bf16* vrow = vt + (db * 32 + lr) * C::VS + kcol;
-            const bf16x4 lo = *(const bf16x4*)vrow;
-            const bf16x4 hi = *(const bf16x4*)(vrow + 8);
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = mfma_bf16(a, pb, o[db]);
-          }
-        }
-    }
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-  }
-
-  // ---- epilogue: O = acc / l, LSE = m + log2(l) in natural-log units --------
-  const float l_tot = sum_halves(l_run);
-  if (myq < N) {
-    const float inv = 1.f / l_tot;
-    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = db * 32 + 8 * a + 4 * g;
-        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
-        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
-      }
-    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
-  }
-}
-
-template <int D, bool CAUSAL, bool FP8, bool PERSIST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_mfma_kernel(FwdParams p) {
-  if constexpr (PERSIST) {
-    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
-    for (int r = 0;; ++r) {
-      const int w = persistent_item(pm, r);
-      if (w < 0) break;
-      fwd_mfma_kernel_item<D, CAUSAL, FP8>(p, item_of(w, p.n_qt));
-    }
-  } else {
-    fwd_mfma_kernel_item<D, CAUSAL, FP8>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
-  }
 }
 
 // ====================================================== bf16, LDS DMA =====
@@ -1229,6 +935,261 @@ void fwd_bf16_pp_kernel(FwdParams p) {
   }
 }
 
+// ================================================ fp8, ping-pong (d = 128) ===
+// The ping-pong kernel's schedule (eight waves, two a SIMD, 256 rows, 64-key
+// tiles) for block-quantised e4m3 inputs: K and V tiles arrive by LDS DMA as
+// fp8 (half the bytes of bf16); S = K Q^T runs on the fp8 MFMA (twice the
+// bf16 rate) with the Q and K block scales folded into the exponent; each
+// phase the workgroup decodes the previous V tile to bf16 once (one 16-byte
+// chunk a thread, exact), behind a second barrier, and P V runs on the bf16
+// MFMA as before, with V's block scale folded into P (P' = P sV, l += sum/sV).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) {
+  constexpr int NW = 8, BR = NW * 32, BC = 64, NKB = BC / 32;
+  constexpr int RB8 = D, RBV = 2 * D;            // bytes per fp8 row, per decoded bf16 row
+  constexpr int T8 = BC * RB8, TV = BC * RBV;
+  constexpr int IPD = T8 / 1024 / NW;            // 1 KB DMA issues per wave per tensor
+  static_assert(IPD == 1 && T8 == NW * 64 * 16, "one 16-byte chunk of a tile per thread");
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[T8];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[T8];
+  __shared__ __attribute__((aligned(1024))) unsigned char r0[T8];
+  __shared__ __attribute__((aligned(1024))) unsigned char r1[T8];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[TV];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[TV];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2;
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const unsigned char* qg = (const unsigned char*)p.q + (size_t)wi.bh * N * D;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * D;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * D;
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + wid * 32;
+  const int myq = q0 + lr;
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  const int nsb = (N + 127) >> 7;                // scale blocks per head
+
+  // Q operand (B of S^T = K Q^T): slot kb <-> columns 64 kb + 32 g .. + 31
+  i32x8 qr[D / 64];
+#pragma unroll
+  for (int kb = 0; kb < D / 64; ++kb) {
+    i32x8 x = {};
+    if (myq < N) {
+      const i32x4* src = (const i32x4*)(qg + (size_t)myq * D + kb * 64 + 32 * g);
+      x = __builtin_shufflevector(src[0], src[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    qr[kb] = x;
+  }
+  // (the wave's rows share one 128-row scale block; rows past N take the last)
+  const float cq = p.scale_log2 * p.qs[(size_t)wi.bh * nsb + (min(q0, N - 1) >> 7)];
+  const float* ksc = p.ks + (size_t)bkv * nsb;
+  const float* vsc = p.vs + (size_t)bkv * nsb;
+
+  const int dma_k0 = dma_base<RB8, kSwzK>(wid * IPD, lane);   // K rows swizzled for the fragment reads
+  const int dma_r0 = wid * 1024 + lane * 16;                   // raw V: a plain copy
+  int koff[D / 64][2];   // K fragment: row lr, 16-byte units 4 kb + 2 g and + 1
+#pragma unroll
+  for (int kb = 0; kb < D / 64; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) koff[kb][hh] = lr * RB8 + k_swz<RB8>(lr, 4 * kb + 2 * g + hh) * 16;
+  constexpr int NVO = D / 32 < 4 ? D / 32 : 4;
+  const int s16 = lane & 15, G = lane >> 4;
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
+  int voff[NVO];
+#pragma unroll
+  for (int db = 0; db < NVO; ++db)
+    voff[db] = vrow * RBV + v_swz<RBV>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+  // decode: this thread's 16 fp8 values (row tid / 8, columns 16 (tid % 8) ..)
+  const int drow = tid >> 3, du = tid & 7;
+  const int dst0 = drow * RBV + v_swz<RBV>(drow, 2 * du) * 16;
+  const int dst1 = drow * RBV + v_swz<RBV>(drow, 2 * du + 1) * 16;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  bf16x8 pk[NKB][2];
+  f32x16 s[NKB];
+
+  auto issue_k = [&](int j, unsigned char* st) {
+    const int key0 = j * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kg + (size_t)key0 * D, min(N - key0, BC) * D);
+    dma16_buf<0>(r, dma_off<RB8, kSwzK>(dma_k0, 0), st + wid * 1024);
+  };
+  auto issue_r = [&](int j, unsigned char* st) {
+    const int key0 = j * BC;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vg + (size_t)key0 * D, min(N - key0, BC) * D);
+    dma16_buf<0>(r, dma_r0, st + wid * 1024);
+  };
+  auto decode = [&](const unsigned char* rl, unsigned char* vl) {
+    const i32x4 x = *(const i32x4*)(rl + tid * 16);
+    i32x4 lo, hi;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      lo[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, false));
+      lo[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, true));
+      hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, false));
+      hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, true));
+    }
+    *(i32x4*)(vl + dst0) = lo;
+    *(i32x4*)(vl + dst1) = hi;
+  };
+  auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {
+    const int key0 = j * BC;
+    if (CAUSAL && key0 > q0 + 31) return false;
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32) s[kb32] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 64; ++kb)
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) {
+        const unsigned char* kr = kl + kb32 * 32 * RB8;
+        const i32x4 a0 = *(const i32x4*)(kr + koff[kb][0]);
+        const i32x4 a1 = *(const i32x4*)(kr + koff[kb][1]);
+        s[kb32] = mfma_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), qr[kb], s[kb32]);
+      }
+    return true;
+  };
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int key0 = j * BC;
+    const float c = cq * ksc[key0 >> 7];
+    const float sv = vsc[key0 >> 7];
+    const float lsv = fast_log2(sv), inv_sv = 1.f / sv;
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
+      const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = kb32 * 32 + 8 * (r >> 2) + (r & 3);
+          if (rel > lim) s[kb32][r] = -INFINITY;
+        }
+    }
+    // P' = P sV against the running max first; the tile max only when some
+    // lane's partial row sum of P leaves [0, kSumBound]
+    auto expo = [&](float m) -> float {
+      float t = 0.f;
+      const float ma = m - lsv;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -ma));
+            const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -ma));
+            w4[w] = pack_bf16(e0, e1);
+            t += e0 + e1;
+          }
+          pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
+        }
+      return t * inv_sv;
+    };
+    float ts = expo(m_run);
+    if (__any(!(ts <= kSumBound))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb32][r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      ts = expo(m_run);
+    }
+    l_run += ts;
+  };
+  auto pv = [&](const unsigned char* vl) {
+#pragma unroll
+    for (int kb32 = 0; kb32 < NKB; ++kb32)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const unsigned char* vb = vl + (kb32 * 32 + 16 * half) * RBV;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const unsigned char* vr = vb + (db / NVO) * 256 + voff[db % NVO];
+          const bf16x4 lo = lds_read_tr16(vr);
+          const bf16x4 hi = lds_read_tr16(vr + 8 * RBV);
+          o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
+        }
+      }
+  };
+
+  // Phase j: K_j in k[j & 1]; the raw V_j in r[j & 1] (loaded in phase j),
+  // decoded in phase j + 1 into v[j & 1] and used there.
+  bool has_s = false, has_p = false;
+  auto step = [&](int j, const unsigned char* kc, unsigned char* kn, unsigned char* r_load,
+                  const unsigned char* r_dec, unsigned char* v_dec) __attribute__((always_inline)) {
+    wait_vmem();
+    barrier_lds();   // K_j and raw V_{j-1} landed; the stages overwritten below are free
+    if (j + 1 < n_tiles) issue_k(j + 1, kn);
+    if (j < n_tiles) issue_r(j, r_load);
+    if (j >= 1) decode(r_dec, v_dec);
+    barrier_lds();   // decoded V_{j-1} visible to every wave
+    if (grp == 1 && has_s) {
+      softmax(j - 1);
+      has_p = true;
+    }
+    if (has_p) pv(v_dec);
+    has_p = false;
+    has_s = j < n_tiles && qk(j, kc);
+    if (grp == 0 && has_s) {
+      softmax(j);
+      has_p = true;
+      has_s = false;
+    }
+  };
+  issue_k(0, k0);
+  for (int j = 0; j <= n_tiles; j += 2) {
+    step(j, k0, k1, r0, r1, v1);
+    if (j + 1 <= n_tiles) step(j + 1, k1, k0, r1, r0, v0);
+  }
+
+  const float l_tot = sum_halves(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = (bf16*)p.o + ((size_t)wi.bh * N + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = db * 32 + 8 * a + 4 * g;
+        const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+        const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        *(i32x2*)(orow + col) = i32x2{(int)lo, (int)hi};
+      }
+    if (p.lse && g == 0) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL, bool PERSIST>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8_pp_kernel(FwdParams p) {
+  if constexpr (PERSIST) {
+    const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
+    for (int r = 0;; ++r) {
+      const int w = persistent_item(pm, r);
+      if (w < 0) break;
+      if (r > 0) __syncthreads();
+      pp8_item<D, CAUSAL>(p, item_of(w, p.n_qt));
+    }
+  } else {
+    pp8_item<D, CAUSAL>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
+  }
+}
+
 // ====================================================== bf16, d = 256 =====
 // Head dim 256: a 32-row block of O alone takes 128 fp32 registers a lane, so
 // one wave per 32 rows cannot run two waves a SIMD.  Here the two waves that
@@ -1787,15 +1748,6 @@ static hipError_t launch_items(KP persistent, KD direct, int threads, FwdParams&
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool FP8>
-static hipError_t launch_mfma(FwdParams& p, hipStream_t s) {
-  // one workgroup per item: the looping instance measured 6% slower on C5
-  finish_grid(p, FwdCfg<D, CAUSAL, FP8>::BR);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, CAUSAL, FP8, false>), dim3(p.total), dim3(FwdCfg<D, CAUSAL, FP8>::NT),
-                     0, s, p);
-  return hipGetLastError();
-}
-
 template <int D, bool CAUSAL, int NW, int BC, int NST>
 static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
   // one workgroup per item: with several workgroups resident per CU the
@@ -1887,8 +1839,17 @@ hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int D, bool CAUSAL>
+static hipError_t launch_pp8(FwdParams& p, hipStream_t s) {
+  finish_grid(p, 256);
+  static std::atomic<int> occ[64];
+  return launch_items(fwd_fp8_pp_kernel<D, CAUSAL, true>, fwd_fp8_pp_kernel<D, CAUSAL, false>, 512, p, s, occ);
+}
+
 hipError_t launch_fwd_fp8(int d, bool causal, FwdParams& p, hipStream_t s) {
-  if (d == 128) return causal ? launch_mfma<128, true, true>(p, s) : launch_mfma<128, false, true>(p, s);
+  // the ping-pong schedule with fp8 K/V tiles (C5 1361 vs 1168 TFLOP/s for a
+  // four-wave kernel that staged the tiles through registers)
+  if (d == 128) return causal ? launch_pp8<128, true>(p, s) : launch_pp8<128, false>(p, s);
   return hipErrorInvalidValue;
 }
 

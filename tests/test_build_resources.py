@@ -26,8 +26,9 @@ def _kernels():
 
 def test_every_kernel_reports_its_resources():
     names = [k["name"] for k in _kernels()]
-    for want in ("fwd_bf16_pp_kernel", "fwd_bf16_pairs_kernel", "fwd_bf16_kernel", "fwd_mfma_kernel",
-                 "fwd_f32_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+    for want in ("fwd_bf16_pp_kernel", "fwd_bf16_pairs_kernel", "fwd_bf16_kernel", "fwd_bf16_sp_kernel",
+                 "fwd_fp8_pp_kernel", "fwd_f32_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+                 "kv_split_kernel", "kv_combine_kernel"):
         assert any(want in n for n in names), want
 
 
@@ -46,5 +47,5 @@ def test_lds_fits_a_compute_unit():
 def test_forward_kernels_keep_two_waves_a_simd():
     # 512 registers a lane per SIMD: two waves need at most 256 each
     for k in _kernels():
-        if "fwd_bf16_pp_kernel" in k["name"] or "fwd_bf16_pairs_kernel" in k["name"]:
+        if any(n in k["name"] for n in ("fwd_bf16_pp_kernel", "fwd_bf16_pairs_kernel", "fwd_fp8_pp_kernel")):
             assert k["vgpr"] <= 256, k
