@@ -22,6 +22,8 @@
 // as zero), row-swizzled so they can be read both as rows (the A operand of
 // Q K^T, dO V^T, K Q^T, V dO^T) and transposed with ds_read_b64_tr_b16 (the A
 // operand of Q^T dS, dO^T P and K^T dS^T) without bank conflicts.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -277,26 +279,37 @@ void bwd_dkdv_kernel(BwdParams p) {
       const int lim = mykey - qq0 - 4 * g;     // query row offset must be >= this
       const int top = MASK ? min(L - 1, W >= 0 ? mykey + W : L - 1) - qq0 - 4 * g : 0;   // ... and <= this
       uint32_t pw[8], sw[8];
+      // (at d = 64, two copies behind a wave-uniform branch: as one, the
+      // compiler turns the mask into a compare and a select per element on
+      // every tile; at d = 128 the second copy costs registers, and spills)
+      auto p_ds = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 lv = *(const f32x4*)(lse2 + qb * 32 + 8 * a4 + 4 * g);
-        const f32x4 dvv = *(const f32x4*)(dl + qb * 32 + 8 * a4 + 4 * g);
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 lv = *(const f32x4*)(lse2 + qb * 32 + 8 * a4 + 4 * g);
+          const f32x4 dvv = *(const f32x4*)(dl + qb * 32 + 8 * a4 + 4 * g);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          float pe[2], se[2];
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float pe[2], se[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 4 * a4 + 2 * h2 + e;
-            float pv = fast_exp2(fmaf(s[r], c, -lv[2 * h2 + e]));
-            if (need_mask && ((CAUSAL && (8 * (r >> 2) + (r & 3)) < lim) ||
-                              (MASK && (8 * (r >> 2) + (r & 3)) > top)))
-              pv = 0.f;
-            pe[e] = pv;
-            se[e] = pv * (dp[r] - dvv[2 * h2 + e]);
+            for (int e = 0; e < 2; ++e) {
+              const int r = 4 * a4 + 2 * h2 + e;
+              float pv = fast_exp2(fmaf(s[r], c, -lv[2 * h2 + e]));
+              if (bool(masked) && ((CAUSAL && (8 * (r >> 2) + (r & 3)) < lim) ||
+                                   (MASK && (8 * (r >> 2) + (r & 3)) > top)))
+                pv = 0.f;
+              pe[e] = pv;
+              se[e] = pv * (dp[r] - dvv[2 * h2 + e]);
+            }
+            pw[2 * a4 + h2] = pack_bf16(pe[0], pe[1]);
+            sw[2 * a4 + h2] = pack_bf16(se[0], se[1]);
           }
-          pw[2 * a4 + h2] = pack_bf16(pe[0], pe[1]);
-          sw[2 * a4 + h2] = pack_bf16(se[0], se[1]);
         }
+      };
+      if constexpr (D <= 64) {
+        if (need_mask) p_ds(std::true_type{});
+        else p_ds(std::false_type{});
+      } else {
+        p_ds(need_mask);
       }
       // ---- dV^T += dO^T P,  dK^T += Q^T dS (transposed operands by tr reads) ---
 #pragma unroll
@@ -486,6 +499,29 @@ void bwd_dq_kernel(BwdParams p) {
                            (MASK && W >= 0 && key0 < q0 + 31 - W);
     const int lim = min(CAUSAL ? myq : L - 1, L - 1) - key0 - 4 * g;
     const int lo = MASK && W >= 0 ? myq - W - key0 - 4 * g : -BC;   // first visible key offset
+    // dS^T = P^T o (dP^T - D) of one 32-key block, packed to bf16 (two copies
+    // behind a wave-uniform branch: as one, the compiler turns the mask into
+    // a compare and a select per element on every tile)
+    auto ds_block = [&](int kb32, const f32x16& s, const f32x16& dp, uint32_t* sw) __attribute__((always_inline)) {
+      auto body = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+          float se[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * r2 + e;
+            float pv = fast_exp2(fmaf(s[r], c, -lse2));
+            if (decltype(masked)::value && ((kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim ||
+                                            (MASK && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) < lo)))
+              pv = 0.f;
+            se[e] = pv * (dp[r] - dlt);
+          }
+          sw[r2] = pack_bf16(se[0], se[1]);
+        }
+      };
+      if (need_mask) body(std::true_type{});
+      else body(std::false_type{});
+    };
     // dS^T of one 32-key block (lane: query column, registers: keys) ...
     auto block_ds = [&](int kb32, bf16x8* ds2) __attribute__((always_inline)) {
       // S^T = K Q^T and dP^T = V dO^T
@@ -498,20 +534,7 @@ void bwd_dq_kernel(BwdParams p) {
         dp = mfma_bf16(av, dor[kb], dp);
       }
       uint32_t sw[8];
-#pragma unroll
-      for (int r2 = 0; r2 < 8; ++r2) {
-        float se[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * r2 + e;
-          float pv = fast_exp2(fmaf(s[r], c, -lse2));
-          if (need_mask && ((kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim ||
-                            (MASK && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) < lo)))
-            pv = 0.f;
-          se[e] = pv * (dp[r] - dlt);
-        }
-        sw[r2] = pack_bf16(se[0], se[1]);
-      }
+      ds_block(kb32, s, dp, sw);
 #pragma unroll
       for (int half = 0; half < 2; ++half)
         ds2[half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
@@ -552,20 +575,7 @@ void bwd_dq_kernel(BwdParams p) {
           dp = mfma_bf16(av, dor[kb], dp);
         }
         uint32_t sw[8];
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) {
-          float se[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * r2 + e;
-            float pv = fast_exp2(fmaf(s[r], c, -lse2));
-            if (need_mask && ((kb32 * 32 + 8 * (r >> 2) + (r & 3)) > lim ||
-                              (MASK && (kb32 * 32 + 8 * (r >> 2) + (r & 3)) < lo)))
-              pv = 0.f;
-            se[e] = pv * (dp[r] - dlt);
-          }
-          sw[r2] = pack_bf16(se[0], se[1]);
-        }
+        ds_block(kb32, s, dp, sw);
 #pragma unroll
         for (int half = 0; half < 2; ++half)
           dsb[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
