@@ -158,6 +158,21 @@ def test_forward_persistent_grid(B, H, N, d, causal):
     assert eo <= TOL["bf16"] and el <= TOL["bf16"], (B, H, N, d, causal, eo, el)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_forward_f32_many_items(causal):
+    """fp32 with more 32-row items than compute units, so the four-wave
+    instance serves it (the small shapes take the eight-wave one); GQA and a
+    ragged last block; every row is compared."""
+    _say(f"fp32 many items causal={causal}")
+    w = syn.Workload("f32m", 2, 160, 40, 300, 64, "f32", causal, 1.0, 57)
+    x = syn.make_inputs(w)
+    o, lse = _run_fwd(x, causal)
+    o_ref, lse_ref = oracle.forward(x["q_64"], x["k_64"], x["v_64"], x["scale"], causal)
+    eo = _err(o.double().cpu().numpy(), o_ref)
+    el = _err(lse.double().cpu().numpy(), lse_ref)
+    assert eo <= TOL["f32"] and el <= TOL["f32"], (causal, eo, el)
+
+
 def test_forward_is_deterministic():
     w = syn.Workload("det", 1, 4, 4, 1000, 128, "bf16", True, 1.0, 3)
     x = syn.make_inputs(w)
