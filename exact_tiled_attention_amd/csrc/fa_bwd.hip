@@ -238,7 +238,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  auto consume = [&](int it_idx, const unsigned char* st) {
+  // MASKED false: a step no query of which precedes a key of the block (no
+  // element needs the mask, so the step carries no mask code at all)
+  auto consume = [&](int it_idx, const unsigned char* st, auto MASKED) __attribute__((always_inline)) {
     int gi, qt;
     step_tile(it_idx, gi, qt);
     const int qrow0 = qt * BQ;
@@ -274,8 +276,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       // ---- P = exp2(S c - LSE2), dS = P (dP - D) -------------------------------
       // (the row statistics are read four rows at a time, as the registers use them)
-      const bool need_mask = (CAUSAL && qq0 < kw0 + 31) ||
-                             (MASK && (qq0 + 31 >= L || (W >= 0 && qq0 + 31 > kw0 + W)));
+      const bool need_mask = bool(MASKED) && ((CAUSAL && qq0 < kw0 + 31) ||
+                                              (MASK && (qq0 + 31 >= L || (W >= 0 && qq0 + 31 > kw0 + W))));
       const int lim = mykey - qq0 - 4 * g;     // query row offset must be >= this
       const int top = MASK ? min(L - 1, W >= 0 ? mykey + W : L - 1) - qq0 - 4 * g : 0;   // ... and <= this
       uint32_t pw[8], sw[8];
@@ -341,30 +343,41 @@ void bwd_dkdv_kernel(BwdParams p) {
       wait_vmem();
       __syncthreads();
       if (nxt < n_iter) issue(nxt, stage1);
-      consume(cur, stage0);
+      consume(cur, stage0, std::true_type{});
       cur = nxt;
       if (cur >= n_iter) break;
       nxt = next_on(cur + 1);
       wait_vmem();
       __syncthreads();
       if (nxt < n_iter) issue(nxt, stage0);
-      consume(cur, stage1);
+      consume(cur, stage1, std::true_type{});
       cur = nxt;
     }
   } else {
-    if (n_iter > 0) issue(0, stage0);
-    for (int it = 0; it < n_iter; it += 2) {
-      wait_vmem();
-      __syncthreads();
-      if (it + 1 < n_iter) issue(it + 1, stage1);
-      consume(it, stage0);
-      if (it + 1 < n_iter) {
+    // Steps from it_split on may hold queries before a key of the block (the
+    // causal diagonal: query tiles at or below qt_m, visited last); the ones
+    // before it run a copy of the step without mask code.  (it_split even, so
+    // both loops start on stage 0.  At d = 128 the second copy spills and
+    // measured 2-4% slower: one loop, masked where needed.)
+    const int qt_m = (k_first + BKV - 2) / BQ;
+    const int it_split = !CAUSAL ? n_iter : D == 128 ? 0 : min(n_iter, max(0, G * (qt_stop - 1 - qt_m))) & ~1;
+    auto run = [&](int it_begin, int it_end, auto MASKED) __attribute__((always_inline)) {
+      for (int it = it_begin; it < it_end; it += 2) {
         wait_vmem();
         __syncthreads();
-        if (it + 2 < n_iter) issue(it + 2, stage0);
-        consume(it + 1, stage1);
+        if (it + 1 < n_iter) issue(it + 1, stage1);
+        consume(it, stage0, MASKED);
+        if (it + 1 < it_end) {
+          wait_vmem();
+          __syncthreads();
+          if (it + 2 < n_iter) issue(it + 2, stage0);
+          consume(it + 1, stage1, MASKED);
+        }
       }
-    }
+    };
+    if (n_iter > 0) issue(0, stage0);
+    run(0, it_split, std::false_type{});
+    run(it_split, n_iter, std::true_type{});
   }
 
   if (MASK && mykey >= L) {
