@@ -173,6 +173,25 @@ def test_forward_f32_many_items(causal):
     assert eo <= TOL["f32"] and el <= TOL["f32"], (causal, eo, el)
 
 
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 1 << 19), ("bf16", 128, 1 << 19), ("f32", 64, 1 << 17)],
+                         ids=lambda v: str(v))
+def test_forward_long_sequence(dtype, d, n):
+    """One head of a very long causal sequence (index arithmetic far beyond the
+    benchmark sizes): sampled rows, the first and last among them, against the
+    oracle's row-by-row computation."""
+    _say(f"long sequence {dtype} d={d} N={n}")
+    w = syn.Workload("long", 1, 1, 1, n, d, dtype, True, 1.0, 90 + d)
+    x = syn.make_inputs(w)
+    o, lse = _run_fwd(x, True)
+    rows = syn.rand_rows(n, 24, seed=d)
+    o = o[0, 0, rows].double().cpu().numpy()
+    lse = lse[0, 0, rows].double().cpu().numpy()
+    o_ref, lse_ref = oracle.forward_rows(x["q_64"][0, 0], x["k_64"][0, 0], x["v_64"][0, 0], x["scale"], True, rows)
+    eo, el = _err(o, o_ref), _err(lse, lse_ref)
+    _say(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL[dtype] and el <= TOL[dtype], (dtype, d, n, eo, el)
+
+
 def test_forward_is_deterministic():
     w = syn.Workload("det", 1, 4, 4, 1000, 128, "bf16", True, 1.0, 3)
     x = syn.make_inputs(w)
