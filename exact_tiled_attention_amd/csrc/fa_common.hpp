@@ -71,11 +71,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-// 16 bytes per lane straight from global memory into LDS (no registers).
-// The destination is wave-uniform: lane l's bytes land at lds + 16*l.
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
 // Transposing LDS read of 16-bit elements.  Within each group of 16 lanes,
 // lane s supplies the address of 4 consecutive elements; lane i receives
 // element (i % 4) of the rows addressed by lanes 4j + i/4, j = 0..3.  With
@@ -102,11 +97,6 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, vo
 // reach ~7.0 TB/s this way against ~6.1 TB/s with the default policy.
 __device__ __forceinline__ void dma16_buf_nt(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voff, 0, 0, 2);
-}
-// l += sum of the two bf16 halves of a packed pair (v_dot2 with (1, 1)).
-__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 // 4 bytes per lane into LDS (lds + 4*l), through a buffer resource.
 __device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, int voff, void* lds_wave_base) {

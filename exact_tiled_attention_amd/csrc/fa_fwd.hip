@@ -43,18 +43,6 @@
 #ifndef FA_NST64
 #define FA_NST64 2
 #endif
-#ifndef FA_BC256
-#define FA_BC256 64
-#endif
-#ifndef FA_NST256
-#define FA_NST256 2
-#endif
-#ifndef FA_D256_PAIRS
-#define FA_D256_PAIRS 1
-#endif
-#ifndef FA_SUM_F32
-#define FA_SUM_F32 1
-#endif
 #ifndef SP_VALU_PER_MFMA
 #define SP_VALU_PER_MFMA 8
 #endif
@@ -262,11 +250,7 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
-#if FA_SUM_F32
             t += e0 + e1;
-#else
-            t = add_bf16_pair(w4[w], t);
-#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
@@ -482,11 +466,7 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
           const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
           const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
           w4[w] = pack_bf16(e0, e1);
-#if FA_SUM_F32
           t += e0 + e1;
-#else
-          t = add_bf16_pair(w4[w], t);
-#endif
         }
         pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
       }
@@ -765,11 +745,7 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
-#if FA_SUM_F32
             t += e0 + e1;
-#else
-            t = add_bf16_pair(w4[w], t);
-#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
@@ -1388,11 +1364,7 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
             const float e0 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w], c, -m));
             const float e1 = fast_exp2(fmaf(s[kb32][half * 8 + 2 * w + 1], c, -m));
             w4[w] = pack_bf16(e0, e1);
-#if FA_SUM_F32
             acc += e0 + e1;
-#else
-            acc = add_bf16_pair(w4[w], acc);
-#endif
           }
           pk[kb32][half] = __builtin_bit_cast(bf16x8, i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]});
         }
@@ -1872,12 +1844,7 @@ hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
       if (p.block_mask)
         return causal ? launch_bf16<128, true, 4, 64, 2>(p, s) : launch_bf16<128, false, 4, 64, 2>(p, s);
       return causal ? launch_pp<128, true, 64, false>(p, s) : launch_pp<128, false, 64, false>(p, s);
-#if FA_D256_PAIRS
     case 256: return causal ? launch_pairs<256, true>(p, s) : launch_pairs<256, false>(p, s);
-#else
-    case 256: return causal ? launch_bf16<256, true, 4, FA_BC256, FA_NST256>(p, s)
-                            : launch_bf16<256, false, 4, FA_BC256, FA_NST256>(p, s);
-#endif
   }
   return hipErrorInvalidValue;
 }
