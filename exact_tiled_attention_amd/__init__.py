@@ -126,6 +126,10 @@ def _stream():
 
 
 def _shape(q, k, v):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d] / [B, H_kv, N, d]")
     B, H, N, d = q.shape
@@ -134,32 +138,113 @@ def _shape(q, k, v):
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    if q.device.index != torch.cuda.current_device():
+        raise ValueError(f"q is on {q.device}, but the current device (whose stream is used) is "
+                         f"cuda:{torch.cuda.current_device()}")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share one dtype")
     return B, H, k.shape[1], N, d
 
 
-def fa_fwd(q, k, v, causal: bool = True, scale: float | None = None,
-           q_descale=None, k_descale=None, v_descale=None, out=None, lse=None,
-           want_lse: bool = True):
-    """O, LSE = attention(q, k, v).  Returns (o, lse); lse is None if not wanted."""
+def _need(t, name, shape, dtype, device):
+    """Check a caller-supplied tensor: exact shape and dtype, contiguous, on
+    `device`.  The C ABI sees only pointers, so a wrong tensor here would be
+    read or written out of bounds (or misread) by the kernels."""
     torch = _torch()
-    lib = load_library()
-    B, H, H_kv, N, d = _shape(q, k, v)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _need_workspace(t, nbytes, device):
+    """A workspace is any contiguous device tensor of at least `nbytes` bytes."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"workspace holds {have} bytes, {nbytes} needed")
+    return t, have
+
+
+def _dtype_code(q):
     codes = DTYPE_CODES()
     if q.dtype not in codes:
         raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
+    return codes[q.dtype]
+
+
+def _out_dtype(dt):
+    torch = _torch()
+    return torch.float32 if dt == FA_DTYPE_F32 else torch.bfloat16
+
+
+def _grads(q, k, v, dq, dk, dv):
+    torch = _torch()
+    dq = torch.empty_like(q) if dq is None else _need(dq, "dq", q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _need(dk, "dk", k.shape, k.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _need(dv, "dv", v.shape, v.dtype, q.device)
+    return dq, dk, dv
+
+
+def _saved(q, o, lse, do, dt):
+    """The backward's saved forward outputs and incoming gradient."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _need(o, "o", (B, H, N, d), _out_dtype(dt), q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    _need(do, "do", (B, H, N, d), _out_dtype(dt), q.device)
+
+
+def _bwd_workspace(lib, workspace, B, H, H_kv, N, d, dt, device):
+    torch = _torch()
+    need = int(lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=device, dtype=torch.uint8)
+    return _need_workspace(workspace, need, device)
+
+
+def fa_fwd(q, k, v, causal: bool = True, scale: float | None = None,
+           q_descale=None, k_descale=None, v_descale=None, out=None, lse=None,
+           want_lse: bool = True):
+    """O, LSE = attention(q, k, v).  Returns (o, lse); lse is None if not wanted.
+
+    fp8 (float8_e4m3fn) inputs need the three fp32 block-scale tensors,
+    q_descale [B, H, ceil(N/128)] and k_descale, v_descale [B, H_kv, ceil(N/128)].
+    """
+    torch = _torch()
+    lib = load_library()
+    B, H, H_kv, N, d = _shape(q, k, v)
+    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out_dtype = torch.float32 if dt == FA_DTYPE_F32 else torch.bfloat16
+    out_dtype = _out_dtype(dt)
     if out is None:
         out = torch.empty(B, H, N, d, device=q.device, dtype=out_dtype)
+    else:
+        _need(out, "out", (B, H, N, d), out_dtype, q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    for t in (q_descale, k_descale, v_descale):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
-            raise ValueError("descale tensors must be contiguous float32")
+    elif lse is not None:
+        _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    if dt == FA_DTYPE_FP8_E4M3:
+        nsb = (N + 127) // 128
+        for name, t, hh in (("q_descale", q_descale, H), ("k_descale", k_descale, H_kv),
+                            ("v_descale", v_descale, H_kv)):
+            if t is not None:
+                _need(t, name, (B, hh, nsb), torch.float32, q.device)
+    elif q_descale is not None or k_descale is not None or v_descale is not None:
+        raise ValueError("descale tensors are only taken with fp8 inputs")
     code = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                       _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
                       B, H, H_kv, N, d, float(scale), int(bool(causal)), dt, _stream())
@@ -174,19 +259,19 @@ def fa_fwd_masked(q, k, v, seqlens=None, window: int | None = None, causal: bool
     torch = _torch()
     lib = load_library()
     B, H, H_kv, N, d = _shape(q, k, v)
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
-    if seqlens is not None and (seqlens.dtype != torch.int32 or not seqlens.is_cuda
-                                or not seqlens.is_contiguous() or tuple(seqlens.shape) != (B,)):
-        raise ValueError("seqlens must be a contiguous int32 device tensor of shape [B]")
+    dt = _dtype_code(q)
+    if seqlens is not None:
+        _need(seqlens, "seqlens", (B,), torch.int32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(B, H, N, d, device=q.device, dtype=torch.bfloat16)
+    else:
+        _need(out, "out", (B, H, N, d), torch.bfloat16, q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    elif lse is not None:
+        _need(lse, "lse", (B, H, N), torch.float32, q.device)
     code = lib.fa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seqlens),
                              -1 if window is None else int(window), B, H, H_kv, N, d, float(scale),
                              int(bool(causal)), dt, _stream())
@@ -196,24 +281,21 @@ def fa_fwd_masked(q, k, v, seqlens=None, window: int | None = None, causal: bool
 
 def fa_bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None,
            workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV of L = sum(O * dO), recomputing P from q, k and the forward's lse."""
-    torch = _torch()
+    """dQ, dK, dV of L = sum(O * dO), recomputing P from q, k and the forward's lse.
+
+    o, lse are the forward's outputs; do has o's shape and dtype.  A supplied
+    workspace is any contiguous device tensor of at least
+    fa_bwd_workspace_bytes(...) bytes."""
     lib = load_library()
     B, H, H_kv, N, d = _shape(q, k, v)
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
+    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    need = int(lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d, dt))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    _saved(q, o, lse, do, dt)
+    dq, dk, dv = _grads(q, k, v, dq, dk, dv)
+    workspace, ws_bytes = _bwd_workspace(lib, workspace, B, H, H_kv, N, d, dt, q.device)
     code = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
                       B, H, H_kv, N, d, float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
@@ -229,6 +311,9 @@ def fa_fwd_kvcache(q, k_cache, v_cache, kv_len=None, causal: bool = True, scale:
     """
     torch = _torch()
     lib = load_library()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("q must be [B, H, N_q, d], the caches [B, H_kv, N_kv, d]")
     B, H, N_q, d = q.shape
@@ -237,28 +322,31 @@ def fa_fwd_kvcache(q, k_cache, v_cache, kv_len=None, causal: bool = True, scale:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k_cache.shape)} "
                          f"v {tuple(v_cache.shape)}")
     for t in (q, k_cache, v_cache):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q and the caches must be contiguous device tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q and the caches must be contiguous tensors on one device")
+    if q.device.index != torch.cuda.current_device():
+        raise ValueError(f"q is on {q.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
         raise ValueError("q and the caches must share one dtype")
-    if kv_len is not None and (kv_len.dtype != torch.int32 or not kv_len.is_cuda
-                               or not kv_len.is_contiguous() or tuple(kv_len.shape) != (B,)):
-        raise ValueError("kv_len must be a contiguous int32 device tensor of shape [B]")
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, q.device)
+    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(B, H, N_q, d, device=q.device, dtype=torch.bfloat16)
+    else:
+        _need(out, "out", (B, H, N_q, d), torch.bfloat16, q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, N_q, device=q.device, dtype=torch.float32)
+    elif lse is not None:
+        _need(lse, "lse", (B, H, N_q), torch.float32, q.device)
     need = int(lib.fa_fwd_kvcache_workspace_bytes(B, H, H_kv, N_q, N_kv, d, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    workspace, ws_bytes = _need_workspace(workspace, need, q.device)
     code = lib.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(out),
-                              _ptr(lse), _ptr(workspace), workspace.numel(), B, H, H_kv, N_q, N_kv,
+                              _ptr(lse), _ptr(workspace), ws_bytes, B, H, H_kv, N_q, N_kv,
                               d, float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return out, lse
@@ -270,35 +358,26 @@ def fa_bwd_masked(q, k, v, o, lse, do, seqlens=None, window: int | None = None, 
     torch = _torch()
     lib = load_library()
     B, H, H_kv, N, d = _shape(q, k, v)
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
-    if seqlens is not None and (seqlens.dtype != torch.int32 or not seqlens.is_cuda
-                                or not seqlens.is_contiguous() or tuple(seqlens.shape) != (B,)):
-        raise ValueError("seqlens must be a contiguous int32 device tensor of shape [B]")
+    dt = _dtype_code(q)
+    if seqlens is not None:
+        _need(seqlens, "seqlens", (B,), torch.int32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    need = int(lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d, dt))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    _saved(q, o, lse, do, dt)
+    dq, dk, dv = _grads(q, k, v, dq, dk, dv)
+    workspace, ws_bytes = _bwd_workspace(lib, workspace, B, H, H_kv, N, d, dt, q.device)
     code = lib.fa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _ptr(seqlens),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _ptr(seqlens),
                              -1 if window is None else int(window), B, H, H_kv, N, d, float(scale),
                              int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
 
 
-def _block_mask_arg(block_mask, H, N):
+def _block_mask_arg(block_mask, H, N, device):
     torch = _torch()
     nb = (N + 127) // 128
-    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous()
-            or tuple(block_mask.shape) != (H, nb, nb)):
-        raise ValueError(f"block_mask must be a contiguous uint8 device tensor of shape [{H}, {nb}, {nb}]")
+    _need(block_mask, "block_mask", (H, nb, nb), torch.uint8, device)
     return _ptr(block_mask)
 
 
@@ -308,18 +387,20 @@ def fa_fwd_blocksparse(q, k, v, block_mask, causal: bool = True, scale: float | 
     torch = _torch()
     lib = load_library()
     B, H, H_kv, N, d = _shape(q, k, v)
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
+    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    bm = _block_mask_arg(block_mask, H, N)
+    bm = _block_mask_arg(block_mask, H, N, q.device)
     if out is None:
         out = torch.empty(B, H, N, d, device=q.device, dtype=torch.bfloat16)
+    else:
+        _need(out, "out", (B, H, N, d), torch.bfloat16, q.device)
     if lse is None and want_lse:
         lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    elif lse is not None:
+        _need(lse, "lse", (B, H, N), torch.float32, q.device)
     code = lib.fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), bm, B, H, H_kv, N, d,
-                                  float(scale), int(bool(causal)), codes[q.dtype], _stream())
+                                  float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return out, lse
 
@@ -327,24 +408,17 @@ def fa_fwd_blocksparse(q, k, v, block_mask, causal: bool = True, scale: float | 
 def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = True, scale: float | None = None,
                        workspace=None, dq=None, dk=None, dv=None):
     """dQ, dK, dV for fa_fwd_blocksparse with the same block mask."""
-    torch = _torch()
     lib = load_library()
     B, H, H_kv, N, d = _shape(q, k, v)
-    codes = DTYPE_CODES()
-    if q.dtype not in codes:
-        raise FaError(3, f"unsupported dtype {q.dtype}")
-    dt = codes[q.dtype]
+    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    bm = _block_mask_arg(block_mask, H, N)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    need = int(lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d, dt))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), device=q.device, dtype=torch.uint8)
+    bm = _block_mask_arg(block_mask, H, N, q.device)
+    _saved(q, o, lse, do, dt)
+    dq, dk, dv = _grads(q, k, v, dq, dk, dv)
+    workspace, ws_bytes = _bwd_workspace(lib, workspace, B, H, H_kv, N, d, dt, q.device)
     code = lib.fa_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                  _ptr(dv), _ptr(workspace), workspace.numel(), bm, B, H, H_kv, N, d,
+                                  _ptr(dv), _ptr(workspace), ws_bytes, bm, B, H, H_kv, N, d,
                                   float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
