@@ -645,7 +645,9 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
   {
     constexpr int RPB = 256 / (D / 8);
     const long rows = (long)p.B * p.H * p.N;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    if (hipError_t e = launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), s, p);
+        e != hipSuccess)
+      return e;
   }
   {
     BwdParams q = p;
@@ -653,7 +655,9 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
     q.total = p.B * p.H_kv * q.n_tiles;
     q.group_items = q.n_tiles;                  // one (batch, K/V head) group per bh
     q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, MASK>), dim3(q.total), dim3(DkdvCfg<D>::NT), 0, s, q);
+    if (hipError_t e = launch_kernel(bwd_dkdv_kernel<D, CAUSAL, MASK>, dim3(q.total), dim3(DkdvCfg<D>::NT), s, q);
+        e != hipSuccess)
+      return e;
   }
   {
     BwdParams q = p;
@@ -661,9 +665,8 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
     q.total = p.B * p.H * q.n_tiles;
     q.group_items = (p.H / p.H_kv) * q.n_tiles;
     q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, MASK>), dim3(q.total), dim3(DqCfg<D>::NT), 0, s, q);
+    return launch_kernel(bwd_dq_kernel<D, CAUSAL, MASK>, dim3(q.total), dim3(DqCfg<D>::NT), s, q);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(int d, bool causal, BwdParams& p, hipStream_t s) {

@@ -31,29 +31,29 @@
 // Causal: key tiles past the work-group's last query are never loaded; the
 // mask is applied only on tiles that straddle the diagonal or the sequence
 // end (FA2's causal optimisation, "Flash Attention 2 / 3 とは 2026年版").
+#include <float.h>
+
 #include <atomic>
 #include <type_traits>
 
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
-#ifndef PV_PREFETCH
-#define PV_PREFETCH 8
-#endif
-#ifndef FA_NST64
-#define FA_NST64 2
-#endif
-#ifndef SP_VALU_PER_MFMA
-#define SP_VALU_PER_MFMA 8
-#endif
-#ifndef FA_PERSIST
-#define FA_PERSIST 1
-#endif
-#ifndef QK_PREFETCH
-#define QK_PREFETCH 8
-#endif
-
 namespace fa {
+
+// Schedule constants, each the best of a sweep on MI355X:
+//  kQkPrefetch   K-fragment LDS reads kept in flight ahead of the MFMA that
+//                uses them (4, 8 and 12 measured within 1% on the d = 128
+//                causal forward);
+//  kPvPrefetch   the same for the transposing V-fragment reads (two a MFMA);
+//  kSpValuPerMfma  VALU instructions the pipelined d = 64 kernel places
+//                between two of its MFMAs;
+//  kNst64        LDS stages of the four-wave d = 64 kernel (four measured
+//                11% slower).
+constexpr int kQkPrefetch = 8;
+constexpr int kPvPrefetch = 8;
+constexpr int kSpValuPerMfma = 8;
+constexpr int kNst64 = 2;
 
 // ------------------------------------------------------ mask variants -----
 // The per-sequence padding mask and the causal sliding window shrink the
@@ -209,17 +209,17 @@ __device__ __forceinline__ void fwd_bf16_kernel_item(const FwdParams& p, const W
       }
       s[kb32] = acc;
     }
-    // Keep QK_PREFETCH K fragments in flight ahead of the MFMA that uses them,
+    // Keep kQkPrefetch K fragments in flight ahead of the MFMA that uses them,
     // so LDS latency overlaps the MFMA chain instead of stalling each step.
     {
       constexpr int NM = (BC / 32) * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkPrefetch, 0);
 #pragma unroll
-      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+      for (int i = 0; i < NM - kQkPrefetch; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kQkPrefetch, 0);
     }
     if ((key0 + BC > L) || (CAUSAL && key0 + BC - 1 > q0) ||
         (MASK && mk.window >= 0 && key0 < q0 + 31 - mk.window)) {
@@ -502,13 +502,13 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
       ts = expo(scur, m_run, pk);
       // the K reads lead; then each MFMA is followed by its share of the VALU
       constexpr int NM = NKB * (D / 16);
-      constexpr int PF = QK_PREFETCH < NM ? QK_PREFETCH : NM;
+      constexpr int PF = kQkPrefetch < NM ? kQkPrefetch : NM;
       __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i + PF < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, SP_VALU_PER_MFMA, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kSpValuPerMfma, 0);
       }
     } else {
       ts = expo(scur, m_run, pk);
@@ -697,13 +697,13 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
       }
     {
       constexpr int NM = NKB * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkPrefetch, 0);
 #pragma unroll
-      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+      for (int i = 0; i < NM - kQkPrefetch; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kQkPrefetch, 0);
     }
     return true;
   };
@@ -788,10 +788,10 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
           o[db] = mfma_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kb32][half], o[db]);
         }
       }
-    // V fragments run PV_PREFETCH reads (two per MFMA) ahead of their MFMA.
+    // V fragments run kPvPrefetch reads (two per MFMA) ahead of their MFMA.
     {
       constexpr int NM = NKB * 2 * (D / 32);
-      constexpr int PF = PV_PREFETCH < 2 * NM ? PV_PREFETCH : 2 * NM;
+      constexpr int PF = kPvPrefetch < 2 * NM ? kPvPrefetch : 2 * NM;
       __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
       for (int i = 0; i < NM - PF / 2; ++i) {
@@ -1033,9 +1033,16 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
   };
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int key0 = j * BC;
-    const float c = cq * ksc[key0 >> 7];
+    // A zero Q or K block scale makes every score of the block 0: the factor
+    // is kept positive (the smallest normal float), so raw scores, whatever
+    // their codes, give exponent arguments of ~0 and masked (-inf) scores stay
+    // -inf instead of 0 * -inf.  A zero V block scale (an all-zero V block)
+    // adds nothing to O but its keys still count in the row sum: P' = 0 and
+    // the sum taken unscaled.  (Block scales are uniform over the wave.)
+    const float c = fmaxf(cq * ksc[key0 >> 7], FLT_MIN);
     const float sv = vsc[key0 >> 7];
-    const float lsv = fast_log2(sv), inv_sv = 1.f / sv;
+    const bool v_zero = !(sv > 0.f);
+    const float lsv = v_zero ? 0.f : fast_log2(sv), inv_sv = v_zero ? 1.f : 1.f / sv;
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
       const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
 #pragma unroll
@@ -1084,6 +1091,10 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       ts = expo(m_run);
+    }
+    if (v_zero) {
+#pragma unroll
+      for (int kb32 = 0; kb32 < NKB; ++kb32) pk[kb32][0] = pk[kb32][1] = bf16x8{};
     }
     l_run += ts;
   };
@@ -1288,13 +1299,13 @@ __device__ __forceinline__ void fwd_bf16_pairs_kernel_item(const FwdParams& p, c
       }
     {
       constexpr int NM = NKB * (D / 16);
-      __builtin_amdgcn_sched_group_barrier(0x100, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkPrefetch, 0);
 #pragma unroll
-      for (int i = 0; i < NM - QK_PREFETCH; ++i) {
+      for (int i = 0; i < NM - kQkPrefetch; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, QK_PREFETCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kQkPrefetch, 0);
     }
   };
   // Bring O and l to the max of the tile about to be added, then add its sums.
@@ -1743,7 +1754,7 @@ static int cu_count() {
 template <typename KP, typename KD>
 static hipError_t launch_items(KP persistent, KD direct, int threads, FwdParams& p, hipStream_t s,
                                std::atomic<int>* occ_cache) {
-  const int cus = FA_PERSIST ? cu_count() : 0;
+  const int cus = cu_count();
   int occ = 0;
   if (cus > 0) {
     int dev = 0;
@@ -1755,12 +1766,8 @@ static hipError_t launch_items(KP persistent, KD direct, int threads, FwdParams&
     }
   }
   const int grid = occ > 0 ? occ * cus : 0;
-  if (grid > 0 && p.total > grid) {
-    hipLaunchKernelGGL(persistent, dim3(grid), dim3(threads), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(direct, dim3(p.total), dim3(threads), 0, s, p);
-  }
-  return hipGetLastError();
+  if (grid > 0 && p.total > grid) return launch_kernel(persistent, dim3(grid), dim3(threads), s, p);
+  return launch_kernel(direct, dim3(p.total), dim3(threads), s, p);
 }
 
 template <int D, bool CAUSAL, int NW, int BC, int NST>
@@ -1770,10 +1777,9 @@ static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
   using C = Bf16Cfg<D, NW, BC, NST>;
   finish_grid(p, C::BR);
   if (masked(p))
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, true>), dim3(p.total), dim3(C::NT), 0, s, p);
+    return launch_kernel(fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, true>, dim3(p.total), dim3(C::NT), s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, false>), dim3(p.total), dim3(C::NT), 0, s, p);
-  return hipGetLastError();
+    return launch_kernel(fwd_bf16_kernel<D, CAUSAL, NW, BC, NST, false, false>, dim3(p.total), dim3(C::NT), s, p);
 }
 
 template <int D, bool CAUSAL>
@@ -1781,8 +1787,7 @@ static hipError_t launch_sp(FwdParams& p, hipStream_t s) {
   // one workgroup per item (two resident per CU)
   using C = Bf16Cfg<D, 4, 64, 2>;
   finish_grid(p, C::BR);
-  hipLaunchKernelGGL((fwd_bf16_sp_kernel<D, CAUSAL>), dim3(p.total), dim3(C::NT), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(fwd_bf16_sp_kernel<D, CAUSAL>, dim3(p.total), dim3(C::NT), s, p);
 }
 
 template <int D, bool CAUSAL>
@@ -1802,10 +1807,9 @@ static hipError_t launch_pairs(FwdParams& p, hipStream_t s) {
                         fwd_bf16_pairs_kernel<D, CAUSAL, false, false>, PairCfg<D>::NT, p, s, occ);
   }
   if (masked(p))
-    hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL, false, true>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
+    return launch_kernel(fwd_bf16_pairs_kernel<D, CAUSAL, false, true>, dim3(p.total), dim3(PairCfg<D>::NT), s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_pairs_kernel<D, CAUSAL, false, false>), dim3(p.total), dim3(PairCfg<D>::NT), 0, s, p);
-  return hipGetLastError();
+    return launch_kernel(fwd_bf16_pairs_kernel<D, CAUSAL, false, false>, dim3(p.total), dim3(PairCfg<D>::NT), s, p);
 }
 
 template <int D, bool CAUSAL, int BC, bool LATE>
@@ -1838,13 +1842,13 @@ hipError_t launch_fwd_bf16(int d, bool causal, FwdParams& p, hipStream_t s) {
   switch (d) {
     case 64:
       if (causal && !masked(p)) return launch_sp<64, true>(p, s);
-      if (p.block_mask && !causal) return launch_bf16<64, false, 4, 64, FA_NST64>(p, s);
+      if (p.block_mask && !causal) return launch_bf16<64, false, 4, 64, kNst64>(p, s);
       // non-causal: the pipelined kernel once its 128-row items exceed what
       // the GPU holds at once (2x16x4096: 899 vs 874 TFLOP/s), the ping-pong
       // kernel below that (C2a_nc, 512 items: 0.145 vs 0.150 ms)
       if (!masked(p) && (long long)p.B * p.H * ((p.N + 127) / 128) > 2LL * cu_count())
         return launch_sp<64, false>(p, s);
-      return causal ? launch_bf16<64, true, 4, 64, FA_NST64>(p, s) : launch_pp<64, false, 128, true>(p, s);
+      return causal ? launch_bf16<64, true, 4, 64, kNst64>(p, s) : launch_pp<64, false, 128, true>(p, s);
     case 128:
       if (p.block_mask)
         return causal ? launch_bf16<128, true, 4, 64, 2>(p, s) : launch_bf16<128, false, 4, 64, 2>(p, s);
@@ -1874,10 +1878,9 @@ static hipError_t launch_f32(FwdParams& p, hipStream_t s) {
   // (C1, 256 items on 256 CUs: 24 us with eight waves, 25 with four; with
   // several items a CU four waves measured 6-16% faster)
   if (p.total <= cu_count())
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, 8>), dim3(p.total), dim3(512), 0, s, p);
+    return launch_kernel(fwd_f32_kernel<D, CAUSAL, 8>, dim3(p.total), dim3(512), s, p);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, 4>), dim3(p.total), dim3(256), 0, s, p);
-  return hipGetLastError();
+    return launch_kernel(fwd_f32_kernel<D, CAUSAL, 4>, dim3(p.total), dim3(256), s, p);
 }
 
 hipError_t launch_fwd_f32(int d, bool causal, FwdParams& p, hipStream_t s) {

@@ -75,6 +75,17 @@ struct KvParams {
   float scale_log2;
 };
 
+// Shape of the decode split kernel per head dim: waves per workgroup and LDS
+// stages (32-key tiles) per wave, sized so one workgroup's stages fill about
+// 128 KB of the CU's 160 KB of LDS; and the fewest 32-key tiles a wave is
+// given (small problems use fewer waves).
+template <int D>
+struct KvCfg;
+template <> struct KvCfg<64> { static constexpr int NW = 4, NST = 4; };
+template <> struct KvCfg<128> { static constexpr int NW = 4, NST = 2; };
+template <> struct KvCfg<256> { static constexpr int NW = 2, NST = 2; };
+constexpr int kKvMinTiles = 2;
+
 // Launch shape and workspace of a KV-cache problem: a pure function of the shape.
 struct KvPlan {
   int G, R, n_rg, R_pad, nw;
@@ -84,6 +95,16 @@ struct KvPlan {
   long long max_tiles; // 32-key tiles of the whole problem at full caches
 };
 KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d);
+
+// Enqueue one kernel on stream s and return that launch's own status.
+// (hipLaunchKernel reports the launch it makes; hipGetLastError after a
+// triple-chevron launch would also return an error left behind by earlier,
+// unrelated work on the calling thread.)
+template <typename P>
+inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s, const P& p) {
+  void* args[] = {const_cast<P*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s);
+}
 
 // Each returns hipSuccess or the launch error; unsupported shapes never reach
 // them (the C ABI validates first).

@@ -38,37 +38,6 @@
 
 namespace fa {
 
-#ifndef FA_KV_NW64
-#define FA_KV_NW64 4
-#endif
-#ifndef FA_KV_NST64
-#define FA_KV_NST64 4
-#endif
-#ifndef FA_KV_NW128
-#define FA_KV_NW128 4
-#endif
-#ifndef FA_KV_NST128
-#define FA_KV_NST128 2
-#endif
-#ifndef FA_KV_NW256
-#define FA_KV_NW256 2
-#endif
-#ifndef FA_KV_NST256
-#define FA_KV_NST256 2
-#endif
-
-// Fewest 32-key tiles a wave is given (small problems use fewer waves).
-#ifndef FA_KV_MIN_TILES
-#define FA_KV_MIN_TILES 2
-#endif
-
-template <int D>
-struct KvCfg;
-// Waves per workgroup and LDS stages per wave, sized so one workgroup's
-// stages fill about 128 KB of the CU's 160 KB of LDS.
-template <> struct KvCfg<64> { static constexpr int NW = FA_KV_NW64, NST = FA_KV_NST64; };
-template <> struct KvCfg<128> { static constexpr int NW = FA_KV_NW128, NST = FA_KV_NST128; };
-template <> struct KvCfg<256> { static constexpr int NW = FA_KV_NW256, NST = FA_KV_NST256; };
 
 template <int D>
 struct KvTile {
@@ -119,7 +88,7 @@ __device__ __forceinline__ KvSplit kv_split(const KvParams& p) {
   if (!p.kv_len) {                             // every cache full: no scan
     KvSplit sp;
     sp.total = p.B * p.upb * ((p.Nkv + 31) >> 5);
-    sp.extra = min(p.W - p.B * p.upb, sp.total / FA_KV_MIN_TILES);
+    sp.extra = min(p.W - p.B * p.upb, sp.total / kKvMinTiles);
     return sp;
   }
   for (int b0 = 0; b0 < p.B; b0 += 64) {
@@ -132,7 +101,7 @@ __device__ __forceinline__ KvSplit kv_split(const KvParams& p) {
   // the same in every lane; readfirstlane lets the compiler keep it in an SGPR
   KvSplit sp;
   sp.total = __builtin_amdgcn_readfirstlane(total);
-  sp.extra = min(p.W - p.B * p.upb, sp.total / FA_KV_MIN_TILES);
+  sp.extra = min(p.W - p.B * p.upb, sp.total / kKvMinTiles);
   return sp;
 }
 __device__ __forceinline__ int pieces_of(const KvSplit& sp, int tiles) {
@@ -469,53 +438,25 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(KvParams p) {
 }
 
 // ------------------------------------------------------------- host -------
-// Waves: one pass of the chip (every resident wave slot of the 256 CUs of
-// MI355X), and at least one per unit; one partial slot per wave.
-KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d) {
-  KvPlan pl{};
-  int nw = 0, nst = 0;
-  switch (d) {
-    case 64: nw = KvCfg<64>::NW; nst = KvCfg<64>::NST; break;
-    case 128: nw = KvCfg<128>::NW; nst = KvCfg<128>::NST; break;
-    case 256: nw = KvCfg<256>::NW; nst = KvCfg<256>::NST; break;
-    default: return pl;
-  }
-  constexpr int kCUs = 256, kLds = 160 * 1024, kBC = 32;
-  const long long wg_lds = (long long)nw * nst * 2 * kBC * d * 2;
-  pl.nw = nw;
-  pl.G = H / H_kv;
-  pl.R = pl.G * Nq;
-  pl.n_rg = (pl.R + 31) / 32;
-  pl.R_pad = pl.R < 32 ? pl.R : 32;
-  const long long units = (long long)B * H_kv * pl.n_rg;
-  long long W = kCUs * (kLds / wg_lds) * nw;
-  if (W < units) W = (units + nw - 1) / nw * nw;
-  pl.W = W;
-  pl.max_tiles = units * ((Nkv + kBC - 1) / kBC);
-  const size_t rows = (size_t)W * pl.R_pad;
-  pl.lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
-  pl.ws_bytes = pl.lse_bytes + rows * d * sizeof(float);
-  return pl;
-}
-
 hipError_t launch_kvcache_bf16(int d, bool causal, KvParams& p, hipStream_t s) {
   const unsigned split_blocks = (unsigned)(p.W / p.nw);
   const unsigned rows = (unsigned)((size_t)p.B * p.H_kv * p.R);
-  auto run = [&](auto dc, auto cc) {
+  auto run = [&](auto dc, auto cc) -> hipError_t {
     constexpr int D = decltype(dc)::value;
     constexpr bool C = decltype(cc)::value;
-    hipLaunchKernelGGL((kv_split_kernel<D, C>), dim3(split_blocks), dim3(KvCfg<D>::NW * 64), 0, s, p);
-    hipLaunchKernelGGL((kv_combine_kernel<D>), dim3(rows), dim3(256), 0, s, p);
+    if (hipError_t e = launch_kernel(kv_split_kernel<D, C>, dim3(split_blocks), dim3(KvCfg<D>::NW * 64), s, p);
+        e != hipSuccess)
+      return e;
+    return launch_kernel(kv_combine_kernel<D>, dim3(rows), dim3(256), s, p);
   };
   using T = std::true_type;
   using F = std::false_type;
   switch (d) {
-    case 64: causal ? run(std::integral_constant<int, 64>{}, T{}) : run(std::integral_constant<int, 64>{}, F{}); break;
-    case 128: causal ? run(std::integral_constant<int, 128>{}, T{}) : run(std::integral_constant<int, 128>{}, F{}); break;
-    case 256: causal ? run(std::integral_constant<int, 256>{}, T{}) : run(std::integral_constant<int, 256>{}, F{}); break;
-    default: return hipErrorInvalidValue;
+    case 64: return causal ? run(std::integral_constant<int, 64>{}, T{}) : run(std::integral_constant<int, 64>{}, F{});
+    case 128: return causal ? run(std::integral_constant<int, 128>{}, T{}) : run(std::integral_constant<int, 128>{}, F{});
+    case 256: return causal ? run(std::integral_constant<int, 256>{}, T{}) : run(std::integral_constant<int, 256>{}, F{});
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -79,7 +79,13 @@ typedef enum {
  *     (b,h,n,:) of a tensor stands for code * descale[b][h][n/128].  This is
  *     the block-wise quantisation with per-tile rescaling that "Flash
  *     Attention 2 / 3 とは 2026年版" names for FP8 attention (section FA3 の
- *     飛躍); the 128-row block is this library's choice.
+ *     飛躍); the 128-row block is this library's choice.  Every descale must
+ *     be finite and >= 0; 0 stands for a block whose values are all zero (as
+ *     an amax/448 quantiser gives an all-zero block), whatever its codes: a
+ *     zero Q or K block gives scores of 0, a zero V block adds nothing to O
+ *     while its keys still count in the softmax sum.  Descales live on the
+ *     device and are not checked: a negative or non-finite one gives
+ *     undefined (typically non-finite) results.
  * Supported: F32 d=64; BF16 d=64,128,256; FP8_E4M3 d=128.  Any N >= 1.
  */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
