@@ -1,24 +1,34 @@
 """Attention throughput on one MI355X: TFLOP/s (causal-adjusted) and % of MFMA peak.
 
-One step = one forward pass over every case of the bf16 forward problem
-(B=1, H=8, N=8192, d=64, causal and non-causal, plus its d=256 variant at
-B=8, H=16, N=2048, causal), inputs resident in HBM.  FLOPs follow the
-standard count: 4*B*H*N^2*d per forward, halved exactly when causal.
+One step = one fp8 forward pass over the largest single-GPU workload: block-
+quantised e4m3 Q/K/V with one fp32 scale per 128-row block, B=1, H=32,
+N=32768, d=128, causal, bf16 output, inputs resident in HBM.  FLOPs follow
+the standard count: 4*B*H*N^2*d per forward, halved exactly when causal
+(2.5x that for a backward).  W untimed warm-up steps, then exactly K steps
+between two device synchronisations; `value` is the step's FLOPs over the
+mean step time, and the per-launch median, p10 and p90 come from HIP events
+on the launching stream.
 
 The JSON line also carries:
-  roofline      the dominant kernel's algorithmic TFLOP/s (from HIP events
-                around each of its launches inside the timed region) against
-                the dense bf16 MFMA peak, and its HBM traffic per launch from
-                the committed rocprofv3 counter summary when that summary was
-                taken on the current kernel source (else null);
+  roofline      the dominant kernel's algorithmic TFLOP/s (FLOPs per launch over
+                its mean launch time from those HIP events) against the dense
+                MFMA peak of its dtype, and its HBM traffic per launch from the
+                committed rocprofv3 counter summary when that summary was taken
+                on the current kernel sources (else null);
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
-                workload on this host's cores;
-  extra         the other kernels measured the same way: the headline-size
-                causal bf16 d=128 forward, the fp32 and fp8 forwards, the
-                bf16 backward (fwd+bwd) at its full size, and the KV-cache
+                workload's inputs (sampled heads and row blocks) on this host's
+                cores, with both the causal-adjusted and the dense FLOP rate;
+  kernel_check  the kernel names of the committed rocprofv3 trace summary of
+                the headline workload, checked against the library's kernels;
+  extra         the other workloads, each with its median (p10, p90) over
+                repetitions that each start with cold caches (a 512 MiB write
+                between repetitions flushes L2 and MALL): the causal bf16 d=128
+                forward at N >= 8192 (with the >= 50% target stated), the five
+                stated problems (fp32, bf16 d=64/256, GQA prefill, training
+                forward + backward), the backward at d=256 and GQA, padded /
+                sliding-window / block-sparse forwards, and the KV-cache
                 (decode) forward as the rate it reads the cache at, against
-                the 8 TB/s HBM peak, and the padded / sliding-window forward
-                (FLOPs of the visible pairs only).
+                the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -35,8 +45,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # dense MFMA, 256 CU x 2.4 GHz
 HBM_GBS = 8000.0
-STEP = ["C2a", "C2a_nc", "C2b"]
-EXTRA_FWD = ["Ta", "Ta_gqa", "Tb", "Tc", "C1", "C3", "C5"]
+HEADLINE = "C5"
+TARGET_SHAPES = ["Ta", "Ta_gqa", "Tb", "Tc"]       # causal bf16, N >= 8192, d = 128
+TARGET_FRAC = 0.5                                  # of the dense bf16 MFMA peak
+EXTRA_FWD = TARGET_SHAPES + ["C1", "C2a", "C2a_nc", "C2b", "C3"]
+FLUSH_BYTES = 512 << 20                            # > the 256 MB MALL + 8 x 4 MB L2
 EXTRA_KV = ["D1", "D1_ragged"]
 EXTRA_MASKED = ["W1", "P1"]
 EXTRA_BLOCKSPARSE = ["S1"]
@@ -64,17 +77,21 @@ def parse():
     ap.add_argument("--with-bwd", action="store_true", help="with --only: also run the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--check-trace", default=None, metavar="CSV",
+                    help="check a rocprofv3 kernel_stats.csv of a bench run (with --only W, or the "
+                         "headline) against the library's kernel names and exit")
     return ap.parse_args()
 
 
 class Case:
     """Device-resident inputs of one workload and a launcher for its kernels."""
 
-    def __init__(self, name, dev, backward=False):
+    def __init__(self, name, dev, backward=False, keep_cpu=False):
         import torch
         import synthetic as syn
         self.w = syn.WORKLOADS[name]
         x = syn.make_inputs(self.w, with_do=backward)
+        self.x = x if keep_cpu else None        # CPU copies (the oracle's inputs)
         self.scale = x["scale"]
         self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
         self.sc = {}
@@ -129,9 +146,10 @@ class KvCase:
         fa.fa_fwd_kvcache(self.q, self.k, self.v, self.kv_len, causal=self.w.causal, scale=self.scale,
                           out=self.o, lse=self.lse, workspace=self.ws)
 
-    def report(self, ms):
+    def report(self, st):
+        ms = st["ms"]
         gbs = self.w.cache_bytes(self.lens) / (ms * 1e-3) / 1e9
-        return {"kernel": f"kvcache_bf16_d{self.w.d}", "ms": round(ms, 4),
+        return {"kernel": f"kvcache_bf16_d{self.w.d}", **st,
                 "cache_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_GBS, 4),
                 "cache_bytes": self.w.cache_bytes(self.lens),
                 "tflops": round(self.w.flops(self.lens) / (ms * 1e-3) / 1e12, 3)}
@@ -157,9 +175,9 @@ class MaskedCase:
         fa.fa_fwd_masked(self.q, self.k, self.v, self.seqlens, self.w.window, causal=self.w.causal,
                          scale=self.scale, out=self.o, lse=self.lse)
 
-    def report(self, ms):
-        tf = self.w.flops_fwd(self.lens) / (ms * 1e-3) / 1e12
-        return {"kernel": f"fwd_bf16_d{self.w.d}_masked", "ms": round(ms, 4), "tflops": round(tf, 2),
+    def report(self, st):
+        tf = self.w.flops_fwd(self.lens) / (st["ms"] * 1e-3) / 1e12
+        return {"kernel": f"fwd_bf16_d{self.w.d}_masked", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "window": self.w.window,
                 "valid_rows": int(sum(self.lens))}
 
@@ -175,9 +193,9 @@ class MaskedCase:
         dq, dk, dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         fn = lambda: fa.fa_bwd_masked(self.q, self.k, self.v, self.o, self.lse, do, self.seqlens, self.w.window,
                                       causal=self.w.causal, scale=self.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
-        ms = median(time_launches(fn, reps=5, warmup=1))
-        tf = 2.5 * self.w.flops_fwd(self.lens) / (ms * 1e-3) / 1e12
-        return {"kernel": f"bwd_bf16_d{self.w.d}_masked", "ms": round(ms, 4), "tflops": round(tf, 2),
+        st = stats(time_launches(fn, reps=5, warmup=1, flush=True))
+        tf = 2.5 * self.w.flops_fwd(self.lens) / (st["ms"] * 1e-3) / 1e12
+        return {"kernel": f"bwd_bf16_d{self.w.d}_masked", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
 
 
@@ -201,9 +219,9 @@ class BlockSparseCase:
         fa.fa_fwd_blocksparse(self.q, self.k, self.v, self.bm, causal=self.w.causal, scale=self.scale,
                               out=self.o, lse=self.lse)
 
-    def report(self, ms):
-        tf = self.w.flops_fwd(self.bm_cpu) / (ms * 1e-3) / 1e12
-        return {"kernel": f"fwd_bf16_d{self.w.d}_blocksparse", "ms": round(ms, 4), "tflops": round(tf, 2),
+    def report(self, st):
+        tf = self.w.flops_fwd(self.bm_cpu) / (st["ms"] * 1e-3) / 1e12
+        return {"kernel": f"fwd_bf16_d{self.w.d}_blocksparse", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "block_density": self.w.density}
 
     def bwd_report(self, dev):
@@ -219,9 +237,9 @@ class BlockSparseCase:
         fn = lambda: fa.fa_bwd_blocksparse(self.q, self.k, self.v, self.o, self.lse, do, self.bm,
                                            causal=self.w.causal, scale=self.scale, workspace=ws,
                                            dq=dq, dk=dk, dv=dv)
-        ms = median(time_launches(fn, reps=5, warmup=1))
-        tf = 2.5 * self.w.flops_fwd(self.bm_cpu) / (ms * 1e-3) / 1e12
-        return {"kernel": f"bwd_bf16_d{self.w.d}_blocksparse", "ms": round(ms, 4), "tflops": round(tf, 2),
+        st = stats(time_launches(fn, reps=5, warmup=1, flush=True))
+        tf = 2.5 * self.w.flops_fwd(self.bm_cpu) / (st["ms"] * 1e-3) / 1e12
+        return {"kernel": f"bwd_bf16_d{self.w.d}_blocksparse", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
 
 
@@ -240,26 +258,66 @@ def kernel_name(w, direction="fwd"):
     return f"fwd_{w.dtype}_d{w.d}_{'causal' if w.causal else 'full'}"
 
 
-def time_launches(fn, reps, warmup):
-    """Per-launch durations (ms) from HIP events on the launching stream."""
+# The library's kernels (the names rocprofv3 shows, without template
+# arguments), and the kernel that dominates each workload's forward in the
+# instance table of fa_fwd.hip / fa_bwd.hip.
+LIB_KERNELS = ("fwd_bf16_kernel", "fwd_bf16_sp_kernel", "fwd_bf16_pp_kernel", "fwd_fp8_pp_kernel",
+               "fwd_bf16_pairs_kernel", "fwd_f32_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel",
+               "bwd_dq_kernel", "kv_split_kernel", "kv_combine_kernel")
+DOMINANT = {"C5": "fa::fwd_fp8_pp_kernel<128, true", "Ta": "fa::fwd_bf16_pp_kernel<128, true",
+            "Ta_gqa": "fa::fwd_bf16_pp_kernel<128, true", "Tb": "fa::fwd_bf16_pp_kernel<128, true",
+            "Tc": "fa::fwd_bf16_pp_kernel<128, true", "C3": "fa::fwd_bf16_pp_kernel<128, true",
+            "C2a": "fa::fwd_bf16_sp_kernel<64, true>", "C2a_nc": "fa::fwd_bf16_pp_kernel<64, false",
+            "C2b": "fa::fwd_bf16_pairs_kernel<256, true", "C1": "fa::fwd_f32_kernel<64, true",
+            "C4": "fa::fwd_bf16_sp_kernel<64, true>"}
+HEADLINE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fp8_d128_causal_C5.md")
+
+
+def time_launches(fn, reps, warmup, flush=False):
+    """Per-launch durations (ms) from HIP events on the launching stream.  With
+    flush, a 512 MiB device write runs between repetitions (outside the
+    events), so every timed launch starts with L2 and MALL holding none of
+    its data."""
     import torch
     for _ in range(warmup):
         fn()
     st = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=torch.device("cuda", torch.cuda.current_device())) \
+        if flush else None
+    out = []
+    for i in range(reps):
+        if buf is not None:
+            buf.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(st)
         fn()
         b.record(st)
+        out.append((a, b))
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    return [a.elapsed_time(b) for a, b in out]
 
 
 def median(xs):
     s = sorted(xs)
     n = len(s)
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def quantile(xs, q):
+    """Linear-interpolated quantile of a sample."""
+    s = sorted(xs)
+    if len(s) == 1:
+        return s[0]
+    pos = q * (len(s) - 1)
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
+
+
+def stats(xs):
+    """Median (the reported time), p10 and p90 of per-launch times in ms."""
+    return {"ms": round(median(xs), 4), "ms_p10": round(quantile(xs, 0.1), 4),
+            "ms_p90": round(quantile(xs, 0.9), 4), "reps": len(xs)}
 
 
 def load_traffic():
@@ -273,47 +331,102 @@ def load_traffic():
     return t.get("kernels", {})
 
 
-def cpu_baseline(budget_s=20.0):
-    """The oracle on a bounded sample: whole rows of the step's workloads."""
+def cpu_baseline(x, w, budget_s=20.0):
+    """The oracle on a bounded sample of the headline workload's own inputs:
+    row blocks of 256 query rows at seeded positions in seeded heads, each
+    row against every key (the oracle forms whole rows of scores, masks them
+    and takes the row softmax).  Reported as TFLOP/s with the metric's count
+    (4 d per visible (query, key) pair), plus the dense rate (4 d per query
+    and key: what the oracle actually computes)."""
     import numpy as np
     import oracle
-    import synthetic as syn
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    flops = 0.0
-    t_total = 0.0
-    done = []
-    per_case = budget_s / len(STEP)
-    for name in STEP:
-        w = syn.WORKLOADS[name]
-        x = syn.make_inputs(w, with_do=False)          # the step's own inputs, as the GPU sees them
-        rows_done = heads = 0
-        t0 = time.perf_counter()
-        for b in range(w.B):
-            for h in range(w.H):
-                if time.perf_counter() - t0 >= per_case:
-                    break
-                kv = oracle.kv_head_of(h, w.H, w.H_kv)
-                rows = np.arange(w.N)
-                oracle.forward_rows(x["q_64"][b, h], x["k_64"][b, kv], x["v_64"][b, kv],
-                                    x["scale"], w.causal, rows)
-                vis = (rows + 1) if w.causal else np.full(rows.size, w.N)
-                flops += float(np.sum(4.0 * w.d * vis))
-                rows_done += rows.size
-                heads += 1
-        t_total += time.perf_counter() - t0
-        done.append(f"{name}: {heads} of {w.B * w.H} heads")
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": "fp64 numpy oracle over whole heads (all rows, all visible keys) of each step "
-                      "workload, heads taken in order until a per-workload time budget; " + "; ".join(done)
-                      + f"; {t_total:.1f} s; TFLOP/s counts 4*d per visible (query,key) pair"}
+    rng = np.random.default_rng(w.seed)
+    rb = 256
+    n_blocks = (w.N + rb - 1) // rb
+    vis = dense = 0.0
+    heads, blocks = set(), 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+        blk = int(rng.integers(n_blocks))
+        rows = np.arange(blk * rb, min(w.N, (blk + 1) * rb))
+        kv = oracle.kv_head_of(h, w.H, w.H_kv)
+        oracle.forward_rows(x["q_64"][b, h], x["k_64"][b, kv], x["v_64"][b, kv], x["scale"], w.causal, rows)
+        vis += float(np.sum(4.0 * w.d * ((rows + 1) if w.causal else np.full(rows.size, w.N))))
+        dense += 4.0 * w.d * rows.size * w.N
+        heads.add((b, h))
+        blocks += 1
+    dt = time.perf_counter() - t0
+    return {"value": vis / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "dense_tflops": dense / dt / 1e12,
+            "sample": f"fp64 numpy oracle on the {w.name} inputs (dequantised fp8 values, as the kernel "
+                      f"sees them): {blocks} blocks of {rb} query rows at seeded positions in "
+                      f"{len(heads)} of {w.B * w.H} heads, {dt:.1f} s; value counts 4*d per visible "
+                      f"(query, key) pair as the metric does ({vis / 1e12:.2f} TFLOP), dense_tflops "
+                      f"4*d per (query, key) pair the oracle computes ({dense / 1e12:.2f} TFLOP)"}
+
+
+def read_summary(path):
+    """(kernel, calls, average us) rows of a committed rocprofv3 trace summary."""
+    rows = []
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("| `"):
+                    cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                    rows.append((cells[0].strip("`"), int(cells[1]), float(cells[2])))
+    except OSError:
+        return []
+    return rows
+
+
+def base_name(kernel):
+    """'void fa::fwd_bf16_pp_kernel<...>(fa::FwdParams)' -> 'fwd_bf16_pp_kernel'."""
+    k = kernel.split("(")[0].split("<")[0].split()[-1]
+    return k.split("::")[-1]
+
+
+def check_kernels(rows, workload):
+    """The trace's kernels by time: every fa:: kernel must be one of the
+    library's, and the dominant one the kernel the instance table picks for
+    the workload.  Returns a dict with ok and the reasons."""
+    want = DOMINANT.get(workload)
+    ours = [r for r in rows if "fa::" in r[0]]
+    problems = []
+    if not ours:
+        problems.append("no fa:: kernel in the trace")
+    for r in ours:
+        if base_name(r[0]) not in LIB_KERNELS:
+            problems.append(f"unknown kernel {r[0]}")
+    top = max(ours, key=lambda r: r[1] * r[2]) if ours else None
+    if want and top and want not in top[0]:
+        problems.append(f"dominant kernel {top[0]} is not {want}")
+    return {"ok": not problems, "expected": want, "dominant": top[0] if top else None,
+            "dominant_avg_us": top[2] if top else None, "problems": problems}
+
+
+def parse_kernel_stats(path):
+    """(kernel, calls, average us) rows of a rocprofv3 kernel_stats.csv."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3))
+    return rows
 
 
 def main():
     args = parse()
+    if args.check_trace:
+        rows = parse_kernel_stats(args.check_trace)
+        res = check_kernels(rows, args.only or HEADLINE)
+        print(json.dumps({"trace": args.check_trace, "workload": args.only or HEADLINE, **res}))
+        sys.exit(0 if res["ok"] else 1)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -337,8 +450,7 @@ def main():
     if args.only in syn.KV_WORKLOADS:
         # decode alone (profiling runs): split + combine kernels per call
         c = KvCase(args.only, dev)
-        xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
-        rep = c.report(median(xs))
+        rep = c.report(stats(time_launches(c.fwd, reps=args.steps, warmup=args.warmup, flush=True)))
         log(f"{args.only}: {rep}")
         print(json.dumps({"metric": "KV-cache read rate (GB/s) of the decode forward",
                           "value": rep["cache_GBps"], "unit": "GB/s", "n_gpus": 1,
@@ -347,153 +459,148 @@ def main():
                           "config": {"workload": args.only}, "decode": rep}))
         return
 
-    if args.only in syn.BLOCKSPARSE_WORKLOADS:
-        c = BlockSparseCase(args.only, dev)
-        rep = c.report(median(time_launches(c.fwd, reps=args.steps, warmup=args.warmup)))
-        rep["bwd"] = c.bwd_report(dev)
-        log(f"{args.only}: {rep}")
-        print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
-                          "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-                          "warmup": args.warmup, "ms_per_step": rep["ms"], "higher_is_better": True,
-                          "dtype": "bf16", "data": "synthetic", "config": {"workload": args.only},
-                          "blocksparse": rep}))
-        return
+    for table, cls in ((syn.BLOCKSPARSE_WORKLOADS, BlockSparseCase), (syn.MASKED_WORKLOADS, MaskedCase)):
+        if args.only in table:
+            c = cls(args.only, dev)
+            rep = c.report(stats(time_launches(c.fwd, reps=args.steps, warmup=args.warmup, flush=True)))
+            rep["bwd"] = c.bwd_report(dev)
+            log(f"{args.only}: {rep}")
+            print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
+                              "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                              "warmup": args.warmup, "ms_per_step": rep["ms"], "higher_is_better": True,
+                              "dtype": "bf16", "data": "synthetic", "config": {"workload": args.only},
+                              "detail": rep}))
+            return
 
-    if args.only in syn.MASKED_WORKLOADS:
-        c = MaskedCase(args.only, dev)
-        xs = time_launches(c.fwd, reps=args.steps, warmup=args.warmup)
-        rep = c.report(median(xs))
-        rep["bwd"] = c.bwd_report(dev)
-        log(f"{args.only}: {rep}")
-        print(json.dumps({"metric": "attention fwd TFLOP/s (visible pairs) and % of MI355X MFMA peak",
-                          "value": rep["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-                          "warmup": args.warmup, "ms_per_step": rep["ms"], "higher_is_better": True,
-                          "dtype": "bf16", "data": "synthetic", "config": {"workload": args.only},
-                          "masked": rep}))
-        return
-
-    names = [args.only] if args.only else STEP
-    cases = [Case(n, dev, backward=(syn_workload(n).backward or args.with_bwd) and bool(args.only)) for n in names]
-    step_flops = sum(c.w.flops_fwd() + (c.w.flops_bwd() if c.backward else 0.0) for c in cases)
-    log(f"timing {args.steps} steps of {names} after {args.warmup} warm-up steps")
+    name = args.only or HEADLINE
+    w0 = syn_workload(name)
+    backward = bool(args.only) and (w0.backward or args.with_bwd)
+    case = Case(name, dev, backward=backward, keep_cpu=not args.only and not args.no_cpu_baseline)
+    step_flops = case.w.flops_fwd() + (case.w.flops_bwd() if backward else 0.0)
+    log(f"timing {args.steps} steps of {name} after {args.warmup} warm-up steps")
 
     for _ in range(args.warmup):
-        for c in cases:
-            c.fwd()
-            if c.backward:
-                c.bwd()
+        case.fwd()
+        if backward:
+            case.bwd()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    per = {}          # (workload, direction) -> per-launch ms
-    ev = []
+    ev = {"fwd": [], "bwd": []}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t_start.record(st)
     for _ in range(args.steps):
-        for c in cases:
-            for direction, fn in (("fwd", c.fwd), ("bwd", c.bwd)):
-                if direction == "bwd" and not c.backward:
-                    continue
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(st)
-                fn()
-                b.record(st)
-                ev.append(((c.w.name, direction), a, b))
+        for direction, fn in (("fwd", case.fwd), ("bwd", case.bwd)):
+            if direction == "bwd" and not backward:
+                continue
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            ev[direction].append((a, b))
     t_end.record(st)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    for key, a, b in ev:
-        per.setdefault(key, []).append(a.elapsed_time(b))
+    per = {k: [a.elapsed_time(b) for a, b in v] for k, v in ev.items() if v}
     ms_per_step = total_ms / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     log(f"{ms_per_step:.4f} ms per step, {value:.1f} TFLOP/s")
 
-    # dominant kernel: the forward launch with the most time inside the timed region
-    by_name = {c.w.name: c for c in cases}
-    fwd_keys = [k for k in per if k[1] == "fwd"]
-    dom_key = max(fwd_keys, key=lambda k: sum(per[k]))
-    dom = by_name[dom_key[0]]
-    dom_ms = sum(per[dom_key]) / len(per[dom_key])
-    achieved = dom.w.flops_fwd() / (dom_ms * 1e-3) / 1e12
-    tr = load_traffic().get(kernel_name(dom.w))
-    traffic = tr["bytes_per_launch"] if tr else None
-    roofline = {"bound": "mfma", "kernel": kernel_name(dom.w), "workload": dom.w.name,
-                "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dom.w.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[dom.w.dtype], 4),
-                "avg_launch_ms": round(dom_ms, 4),
-                "traffic": traffic,
-                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+    fwd_ms = sum(per["fwd"]) / len(per["fwd"])
+    achieved = case.w.flops_fwd() / (fwd_ms * 1e-3) / 1e12
+    tr = load_traffic().get(kernel_name(case.w))
+    peak = PEAK_TFLOPS[case.w.dtype]
+    roofline = {"bound": "mfma", "kernel": kernel_name(case.w), "workload": name,
+                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "avg_launch_ms": round(fwd_ms, 4),
+                "traffic": tr["bytes_per_launch"] if tr else None,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "traffic_detail": tr}
-    cases_out = {}
-    for (name, direction), xs in per.items():
-        w = by_name[name].w
-        fl = w.flops_fwd() if direction == "fwd" else w.flops_bwd()
-        cases_out[f"{name}.{direction}"] = {"ms_median": round(median(xs), 4),
-                                            "tflops": round(fl / (median(xs) * 1e-3) / 1e12, 2)}
+    if case.w.dtype == "fp8":
+        # the PV product runs on the bf16 MFMA: 2/3 of the fp8 peak is the most
+        # an fp8 QK^T + bf16 PV split can reach
+        roofline["note"] = "QK^T on fp8 MFMA, PV on bf16 MFMA"
+    timing = {d_: {**stats(v), "tflops": round((case.w.flops_fwd() if d_ == "fwd" else case.w.flops_bwd())
+                                               / (median(v) * 1e-3) / 1e12, 2)} for d_, v in per.items()}
+
+    kcheck = None
+    if not args.only:
+        rows = read_summary(HEADLINE_SUMMARY)
+        kcheck = check_kernels(rows, name)
+        kcheck["summary"] = os.path.relpath(HEADLINE_SUMMARY, ROOT)
+        if kcheck["dominant_avg_us"]:
+            kcheck["live_avg_us"] = round(fwd_ms * 1e3, 1)
+            kcheck["live_over_summary"] = round(fwd_ms * 1e3 / kcheck["dominant_avg_us"], 3)
+        log(f"kernel check: {kcheck}")
+
+    cpu = None
+    if not args.only and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(case.x, case.w)
+    del case
+    torch.cuda.empty_cache()
 
     extra = {}
     if not args.no_extra and not args.only:
-        del cases
-        torch.cuda.empty_cache()
-        for name in EXTRA_FWD:
-            log(f"extra: {name}")
-            c = Case(name, dev)
-            ms = median(time_launches(c.fwd, reps=10, warmup=2))
-            tf = c.w.flops_fwd() / (ms * 1e-3) / 1e12
-            extra[name] = {"kernel": kernel_name(c.w), "ms": round(ms, 4), "tflops": round(tf, 2),
-                           "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
+        for nm in EXTRA_FWD:
+            log(f"extra: {nm}")
+            c = Case(nm, dev)
+            s_ = stats(time_launches(c.fwd, reps=10, warmup=2, flush=True))
+            tf = c.w.flops_fwd() / (s_["ms"] * 1e-3) / 1e12
+            extra[nm] = {"kernel": kernel_name(c.w), **s_, "tflops": round(tf, 2),
+                         "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
             del c
             torch.cuda.empty_cache()
-        for name in EXTRA_MASKED:
-            log(f"extra: {name}")
-            c = MaskedCase(name, dev)
-            extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
-            if name == "W1":
-                extra[name + ".bwd"] = c.bwd_report(dev)
+        fr = {nm: extra[nm]["frac_peak"] for nm in TARGET_SHAPES}
+        extra["target"] = {"what": "causal bf16 forward, N >= 8192, d = 128, fraction of the dense bf16 "
+                                   "MFMA peak at every shape", "shapes": fr, "target_min_frac": TARGET_FRAC,
+                           "min_frac": min(fr.values()), "met": min(fr.values()) >= TARGET_FRAC}
+        for nm in EXTRA_MASKED:
+            log(f"extra: {nm}")
+            c = MaskedCase(nm, dev)
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=10, warmup=2, flush=True)))
+            if nm == "W1":
+                extra[nm + ".bwd"] = c.bwd_report(dev)
             del c
             torch.cuda.empty_cache()
-        for name in EXTRA_BLOCKSPARSE:
-            log(f"extra: {name}")
-            c = BlockSparseCase(name, dev)
-            extra[name] = c.report(median(time_launches(c.fwd, reps=10, warmup=2)))
-            extra[name]["bwd"] = c.bwd_report(dev)
+        for nm in EXTRA_BLOCKSPARSE:
+            log(f"extra: {nm}")
+            c = BlockSparseCase(nm, dev)
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=10, warmup=2, flush=True)))
+            extra[nm]["bwd"] = c.bwd_report(dev)
             del c
             torch.cuda.empty_cache()
-        for name in EXTRA_KV:
-            log(f"extra: {name}")
-            c = KvCase(name, dev)
-            extra[name] = c.report(median(time_launches(c.fwd, reps=20, warmup=3)))
+        for nm in EXTRA_KV:
+            log(f"extra: {nm}")
+            c = KvCase(nm, dev)
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=20, warmup=3, flush=True)))
             del c
             torch.cuda.empty_cache()
-        for name in ("C2b", "C3"):
-            log(f"extra: {name} backward")
-            c = Case(name, dev, backward=True)
+        for nm in ("C2b", "C3"):
+            log(f"extra: {nm} backward")
+            c = Case(nm, dev, backward=True)
             c.fwd()
-            ms_b = median(time_launches(c.bwd, reps=5, warmup=1))
-            tf = c.w.flops_bwd() / (ms_b * 1e-3) / 1e12
-            extra[name + ".bwd"] = {"kernel": kernel_name(c.w, "bwd"), "ms": round(ms_b, 4), "tflops": round(tf, 2),
-                                    "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+            s_ = stats(time_launches(c.bwd, reps=5, warmup=1, flush=True))
+            tf = c.w.flops_bwd() / (s_["ms"] * 1e-3) / 1e12
+            extra[nm + ".bwd"] = {"kernel": kernel_name(c.w, "bwd"), **s_, "tflops": round(tf, 2),
+                                  "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
             del c
             torch.cuda.empty_cache()
         log("extra: C4 forward + backward")
         c = Case("C4", dev, backward=True)
-        ms_f = median(time_launches(c.fwd, reps=10, warmup=2))
-        ms_b = median(time_launches(c.bwd, reps=10, warmup=2))
-        extra["C4"] = {"fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
-                       "fwd_tflops": round(c.w.flops_fwd() / (ms_f * 1e-3) / 1e12, 2),
-                       "bwd_tflops": round(c.w.flops_bwd() / (ms_b * 1e-3) / 1e12, 2),
+        sf = stats(time_launches(c.fwd, reps=10, warmup=2, flush=True))
+        sb = stats(time_launches(c.bwd, reps=10, warmup=2, flush=True))
+        extra["C4"] = {"fwd": {**sf, "tflops": round(c.w.flops_fwd() / (sf["ms"] * 1e-3) / 1e12, 2)},
+                       "bwd": {**sb, "tflops": round(c.w.flops_bwd() / (sb["ms"] * 1e-3) / 1e12, 2)},
                        "fwd_bwd_tflops": round((c.w.flops_fwd() + c.w.flops_bwd())
-                                               / ((ms_f + ms_b) * 1e-3) / 1e12, 2),
-                       "bwd_frac_peak": round(c.w.flops_bwd() / (ms_b * 1e-3) / 1e12
+                                               / ((sf["ms"] + sb["ms"]) * 1e-3) / 1e12, 2),
+                       "bwd_frac_peak": round(c.w.flops_bwd() / (sb["ms"] * 1e-3) / 1e12
                                               / PEAK_TFLOPS["bf16"], 4)}
         del c
         torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu_baseline and not args.only:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline()
-
+    w = syn_workload(name)
     out = {
         "metric": "attention fwd/bwd TFLOP/s (causal-adjusted) and % of MI355X MFMA peak",
         "value": round(value, 2),
@@ -505,14 +612,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cases[0].w.dtype if args.only else "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, bf16 RNE)",
-        "config": {"workload": "bf16 forward: B=1,H=8,N=8192,d=64 causal + non-causal; "
-                               "B=8,H=16,N=2048,d=256 causal" if not args.only else args.only,
-                   "cases": cases_out, "frac_of_bf16_peak": round(value / PEAK_TFLOPS["bf16"], 4),
-                   "parallelism": "single GPU"},
+        "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.dtype],
+        "data": ("synthetic: seeded N(0,1) Q/K/V, block-quantised to OCP e4m3 with one fp32 scale "
+                 "per 128-row block" if w.dtype == "fp8" else "synthetic: seeded N(0,1) Q/K/V"),
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "dtype_in": w.dtype, "out": "f32" if w.dtype == "f32" else "bf16",
+                   "backward": backward, "timing": timing,
+                   "frac_of_peak": round(value / PEAK_TFLOPS[w.dtype], 4), "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "kernel_check": kcheck,
         "extra": extra,
         "source_hash": source_hash(),
     }
