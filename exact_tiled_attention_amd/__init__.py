@@ -15,7 +15,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_masked", "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+__all__ = ["fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_masked",
+           "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
            "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
            "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
 
@@ -25,7 +26,8 @@ FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE",
                 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_INVALID_VALUE", 5: "FA_ERR_WORKSPACE",
                 6: "FA_ERR_HIP"}
-EXPORTED = ("fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_masked", "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
+EXPORTED = ("fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_masked",
+            "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
             "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
             "fa_status_string")
 
@@ -57,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd_masked.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_masked.restype = i
     lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
@@ -297,6 +301,26 @@ def fa_bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None,
     code = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
                       B, H, H_kv, N, d, float(scale), int(bool(causal)), dt, _stream())
+    _check(code)
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None,
+                   dq=None, dk=None, dv=None):
+    """fa_bwd without a workspace: the library's static device scratch holds
+    the per-row statistics (fa_bwd_workspace_bytes must be <= 16 MiB).  Calls
+    that overlap on one GPU race (they share that scratch).  Allocates only
+    the gradients, and nothing when dq, dk and dv are given."""
+    lib = load_library()
+    B, H, H_kv, N, d = _shape(q, k, v)
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _saved(q, o, lse, do, dt)
+    dq, dk, dv = _grads(q, k, v, dq, dk, dv)
+    code = lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, H_kv, N, d, float(scale),
+                              int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
 

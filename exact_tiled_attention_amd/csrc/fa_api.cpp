@@ -62,7 +62,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: non-positive size, H not a multiple of H_kv, or size overflow";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this (dtype, head dim, direction)";
     case FA_ERR_INVALID_VALUE: return "FA_ERR_INVALID_VALUE: scale not finite and positive, misaligned pointer, aliasing output, or misplaced descale";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small (fa_bwd_noalloc: the problem needs more than its static scratch)";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error at launch";
   }
   return "unknown fa_status";
@@ -179,11 +179,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, fa_dtype dty
   return 2 * row_stats;   // D = rowsum(dO * O), then LSE in base-2 units
 }
 
+// Validation and launch of every backward entry point.  With `noalloc` the
+// workspace arguments are ignored: the statistics go to the library's static
+// device scratch, after the same checks (and the size limit of the scratch).
 static fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                             const void* dO, void* dQ, void* dK, void* dV, void* workspace,
                             size_t workspace_bytes, const int* seqlens, int window,
                             const unsigned char* block_mask, int B, int H, int H_kv,
-                            int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+                            int N, int d, float scale, int causal, fa_dtype dtype, hipStream_t stream,
+                            bool noalloc = false) {
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL_POINTER;
   if (!valid_dtype(dtype)) return FA_ERR_UNSUPPORTED;
   if (fa_status s = check_shape(B, H, H_kv, N, d); s != FA_OK) return s;
@@ -195,8 +199,13 @@ static fa_status bwd_common(const void* Q, const void* K, const void* V, const v
     if (!aligned16(q)) return FA_ERR_INVALID_VALUE;
   if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return FA_ERR_INVALID_VALUE;
   const size_t need = fa_bwd_workspace_bytes(B, H, H_kv, N, d, dtype);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  if (noalloc) {
+    if (need > fa::kBwdScratchBytes) return FA_ERR_WORKSPACE;
+    workspace = nullptr;   // resolved below, after every check
+    workspace_bytes = need;
+  } else if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)) {
     return FA_ERR_WORKSPACE;
+  }
   const size_t eb = elem_bytes(dtype);
   const size_t nq = (size_t)B * H * N * d * eb, nkv = (size_t)B * H_kv * N * d * eb;
   const size_t nl = (size_t)B * H * N * 4;
@@ -212,6 +221,8 @@ static fa_status bwd_common(const void* Q, const void* K, const void* V, const v
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_VALUE;
   }
+
+  if (noalloc && fa::bwd_scratch(&workspace) != hipSuccess) return FA_ERR_HIP;
 
   fa::BwdParams p{};
   p.q = Q; p.k = K; p.v = V; p.o = O; p.lse = LSE; p.dout = dO;
@@ -235,6 +246,13 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int causal, fa_dtype dtype, hipStream_t stream) {
   return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, -1, nullptr, B, H,
                     H_kv, N, d, scale, causal, dtype, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                         const void* dO, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N, int d,
+                         float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, nullptr, 0, nullptr, -1, nullptr, B, H, H_kv, N, d, scale,
+                    causal, dtype, stream, /*noalloc=*/true);
 }
 
 fa_status fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const float* LSE,

@@ -22,6 +22,7 @@
 // as zero), row-swizzled so they can be read both as rows (the A operand of
 // Q K^T, dO V^T, K Q^T, V dO^T) and transposed with ds_read_b64_tr_b16 (the A
 // operand of Q^T dS, dO^T P and K^T dS^T) without bank conflicts.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -29,6 +30,33 @@
 
 
 namespace fa {
+
+// ====================================================== static scratch ===
+// Device memory of fa_bwd_noalloc: the backward's per-row statistics (D and
+// the base-2 LSE, kBwdScratchBytes at most) live in this file-scope array
+// instead of a caller workspace.  Each GPU holds its own copy for as long as
+// the process runs, and every call on that GPU shares it, so calls that
+// overlap on one GPU race.  Nothing in it needs clearing: the prep kernel
+// writes every row the other two kernels read.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+// Device address of this GPU's copy.  In host code `scratch` names a host-side
+// stand-in, not device memory, so kernels get the address from
+// hipGetSymbolAddress, looked up once per device with that device current.
+hipError_t bwd_scratch(void** ptr) {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 // ============================================================ prep ======
 template <int D>

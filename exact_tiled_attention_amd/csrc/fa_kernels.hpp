@@ -96,6 +96,11 @@ struct KvPlan {
 };
 KvPlan kv_plan(int B, int H, int H_kv, int Nq, int Nkv, int d);
 
+// Size of the static device scratch behind fa_bwd_noalloc (per GPU), and the
+// lookup of its device address on the current device.
+constexpr size_t kBwdScratchBytes = 16u << 20;
+hipError_t bwd_scratch(void** ptr);
+
 // Enqueue one kernel on stream s and return that launch's own status.
 // (hipLaunchKernel reports the launch it makes; hipGetLastError after a
 // triple-chevron launch would also return an error left behind by earlier,

@@ -170,6 +170,26 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int causal, fa_dtype dtype, hipStream_t stream);
 
 /*
+ * fa_bwd without a workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments, results and errors are those of fa_bwd; the
+ * per-row statistics go to a static device array of the library instead of a
+ * caller workspace.  Nothing is allocated or freed by the call.
+ *   Limit: fa_bwd_workspace_bytes(B, H, H_kv, N, d, dtype) <= 16 MiB
+ *     (16777216 bytes; B * H * N <= 2^21 rows); larger problems return
+ *     FA_ERR_WORKSPACE.
+ *   Each GPU the library runs on holds its own 16 MiB array until the
+ *   process ends.  Every call on one GPU uses that same array, so calls that
+ *   overlap in time on one GPU (concurrent streams, or threads) race and
+ *   must be serialised by the caller; calls on different GPUs do not share
+ *   it.  Its contents between calls are meaningless.
+ *   FA_ERR_HIP also covers a failed lookup of the array's device address.
+ */
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                         const void* dO, void* dQ, void* dK, void* dV, int B, int H, int H_kv, int N,
+                         int d, float scale, int causal, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_fwd_kvcache needs for this problem (0 on
  * invalid arguments or an unsupported (dtype, d)).  A pure function of its
  * arguments.

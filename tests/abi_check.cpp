@@ -27,6 +27,8 @@ hipError_t launch_fwd_bf16(int, bool, FwdParams& p, hipStream_t) { ++g_calls; g_
 hipError_t launch_fwd_fp8(int, bool, FwdParams& p, hipStream_t) { ++g_calls; g_last = "fwd_fp8"; g_fwd = p; return g_result; }
 hipError_t launch_bwd_bf16(int, bool, BwdParams& p, hipStream_t) { ++g_calls; g_last = "bwd_bf16"; g_bwd = p; return g_result; }
 hipError_t launch_kvcache_bf16(int, bool, KvParams& p, hipStream_t) { ++g_calls; g_last = "kvcache"; g_kv = p; return g_result; }
+static int g_scratch_lookups = 0;
+hipError_t bwd_scratch(void** ptr) { ++g_scratch_lookups; *ptr = reinterpret_cast<void*>((uintptr_t)77 << 32); return hipSuccess; }
 }  // namespace fa
 
 static int failures = 0;
@@ -176,6 +178,26 @@ static void check_backward() {
                             nullptr) == FA_ERR_INVALID_SHAPE);
 }
 
+static void check_noalloc() {
+  // the static scratch replaces the workspace; problems beyond it are refused
+  fa::g_calls = 0;
+  fa::g_scratch_lookups = 0;
+  EXPECT(fa_bwd_noalloc(A(0), A(1), A(2), A(3), (const float*)A(4), A(5), A(6), A(7), A(8), 2, 4, 2, 300, 64,
+                        0.125f, 1, FA_DTYPE_BF16, nullptr) == FA_OK);
+  EXPECT(fa::g_calls == 1 && fa::g_scratch_lookups == 1);
+  EXPECT(fa::g_bwd.delta == (float*)((uintptr_t)77 << 32));
+  EXPECT(fa_bwd_workspace_bytes(1, 1, 1, 1 << 21, 64, FA_DTYPE_BF16) <= fa::kBwdScratchBytes);
+  EXPECT(fa_bwd_noalloc(A(0), A(1), A(2), A(3), (const float*)A(4), A(5), A(6), A(7), A(8), 1, 1, 1, 1 << 21,
+                        64, 0.125f, 1, FA_DTYPE_BF16, nullptr) == FA_OK);
+  EXPECT(fa_bwd_noalloc(A(0), A(1), A(2), A(3), (const float*)A(4), A(5), A(6), A(7), A(8), 1, 1, 1,
+                        (1 << 21) + 1, 64, 0.125f, 1, FA_DTYPE_BF16, nullptr) == FA_ERR_WORKSPACE);
+  EXPECT(fa_bwd_noalloc(A(0), A(1), A(2), A(3), (const float*)A(4), A(5), A(6), A(7), A(8), 2, 4, 2, 300, 128,
+                        0.125f, 1, FA_DTYPE_FP8_E4M3, nullptr) == FA_ERR_UNSUPPORTED);
+  EXPECT(fa_bwd_noalloc(A(0), A(1), A(2), A(3), (const float*)A(4), A(5), A(0), A(7), A(8), 2, 4, 2, 300, 64,
+                        0.125f, 1, FA_DTYPE_BF16, nullptr) == FA_ERR_INVALID_VALUE);
+  EXPECT(fa::g_calls == 2 && fa::g_scratch_lookups == 2);      // refused calls look nothing up
+}
+
 static void check_kvcache() {
   const size_t need = fa_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128, FA_DTYPE_BF16);
   EXPECT(need > 0 && need == fa_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128, FA_DTYPE_BF16));
@@ -207,6 +229,7 @@ int main() {
   check_forward();
   check_masked_and_sparse();
   check_backward();
+  check_noalloc();
   check_kvcache();
   check_strings();
   if (failures) {
