@@ -846,15 +846,29 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   } else {
   // K_j lives in stage j % 2 of k, V_j in stage j % 2 of v; phase j loads
   // K_{j+1} and V_j.
+  //
+  // Issuing a DMA stalls the wave while the CU's texture path takes the
+  // copies in (~300-500 clocks for a phase's 32 KB when every wave issues at
+  // once).  Group 1's phase is the longer one (softmax, then its 32
+  // products), so it issues its share after its softmax, where the copies
+  // of group 0 have gone and its products wait for the matrix pipe anyway
+  // (C3 0.595 -> 0.526 ms, Ta -3%; issuing later still, between its two
+  // product blocks, left too little time for the copies to land: Tc +6%).
   auto step = [&](int j, const unsigned char* kc, const unsigned char* vp, unsigned char* kn,
                   unsigned char* vn) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
-    if (j + 1 < n_tiles) issue_one(kg, dma_k, j + 1, kn);
-    if (j < n_tiles) issue_one(vg, dma_v, j, vn);
+    if (grp == 0) {
+      if (j + 1 < n_tiles) issue_one(kg, dma_k, j + 1, kn);
+      if (j < n_tiles) issue_one(vg, dma_v, j, vn);
+    }
     if (grp == 1 && has_s) {
       softmax(j - 1);
       has_p = true;
+    }
+    if (grp == 1) {
+      if (j + 1 < n_tiles) issue_one(kg, dma_k, j + 1, kn);
+      if (j < n_tiles) issue_one(vg, dma_v, j, vn);
     }
     if (has_p) pv(vp);
     has_p = false;
@@ -1031,6 +1045,8 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
       }
     return true;
   };
+  // (block scales of the wave's next softmax tile, loaded one softmax ahead)
+  float ks_cur = ksc[0], vs_cur = vsc[0];
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int key0 = j * BC;
     // A zero Q or K block scale makes every score of the block 0: the factor
@@ -1039,8 +1055,13 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
     // -inf instead of 0 * -inf.  A zero V block scale (an all-zero V block)
     // adds nothing to O but its keys still count in the row sum: P' = 0 and
     // the sum taken unscaled.  (Block scales are uniform over the wave.)
-    const float c = fmaxf(cq * ksc[key0 >> 7], FLT_MIN);
-    const float sv = vsc[key0 >> 7];
+    const float c = fmaxf(cq * ks_cur, FLT_MIN);
+    const float sv = vs_cur;
+    {
+      const int kn = min(j + 1, n_tiles - 1) * BC;
+      ks_cur = ksc[kn >> 7];
+      vs_cur = vsc[kn >> 7];
+    }
     const bool v_zero = !(sv > 0.f);
     const float lsv = v_zero ? 0.f : fast_log2(sv), inv_sv = v_zero ? 1.f : 1.f / sv;
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0)) {
