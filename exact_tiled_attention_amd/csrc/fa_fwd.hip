@@ -54,6 +54,10 @@ constexpr int kQkPrefetch = 8;
 constexpr int kPvPrefetch = 8;
 constexpr int kSpValuPerMfma = 8;
 constexpr int kNst64 = 2;
+// fp8 forward: which waves copy the K and raw V tiles and decode V (1: group
+// 0 copies, group 1 decodes after its softmax; 2: group 0 does both; 3: all
+// waves do both at the top of the phase).
+constexpr int kFp8Plan = 1;
 
 // ------------------------------------------------------ mask variants -----
 // The per-sequence padding mask and the causal sliding window shrink the
@@ -367,10 +371,21 @@ void fwd_bf16_kernel(FwdParams p) {
 // No tile is skipped for a wave (a tile past the wave's rows is masked out
 // instead), so every step has the same shape.  Every row sees a key of its
 // first tile (no mask but the causal one), which the lazy max relies on.
-template <int D, bool CAUSAL>
+//
+// With SPLIT the workgroup owns 64 rows, and its waves split the keys: waves
+// 0 and 1 (rows 0-31 and 32-63 of the item) take the even 64-key tiles,
+// waves 2 and 3 the odd ones; a step loads a pair of tiles and each wave
+// works on its half.  At the end the odd waves hand their running max, sum
+// and O to their partners through LDS, which merge them with the same
+// rescaling as between tiles.  Twice the items, each half as long per wave:
+// when a short causal grid has about as many items as resident workgroups
+// the longest items no longer leave most of the GPU idle at the end.
+template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkItem wi) {
-  using C = Bf16Cfg<D, 4, 64, 2>;
-  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPW = C::IPW, NKB = BC / 32;
+  using C = Bf16Cfg<D, 4, SPLIT ? 128 : 64, 2>;
+  constexpr int BC = 64, RB = C::RB, IPW = C::IPW, NKB = BC / 32;
+  constexpr int BR = SPLIT ? 64 : C::BR;   // rows per item
+  constexpr int BT = C::BC;                // keys loaded per step
   __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILE];
@@ -386,11 +401,14 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
   const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
   const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
   const int q_first = wi.qt * BR;
-  const int q0 = q_first + wid * 32;
+  const int rb = SPLIT ? (wid & 1) : wid;  // this wave's 32-row block of the item
+  const int par = SPLIT ? (wid >> 1) : 0;  // (SPLIT) which 64-key half of a step
+  const int q0 = q_first + rb * 32;
   const int myq = q0 + lr;
   const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  auto key_of = [&](int j) -> int { return j * BC; };
+  const int n_tiles = (kv_end + BT - 1) / BT;   // steps
+  auto key_of = [&](int j) -> int { return j * BT + par * BC; };   // this wave's first key of step j
+  const int hoff = par * BC * RB;                                    // its half of a stage
 
   bf16x8 qr[D / 16];
 #pragma unroll
@@ -425,8 +443,8 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
   float m_run = -INFINITY, l_run = 0.f;
 
   auto issue = [&](const unsigned char* src, const int* off, int j, unsigned char* st) {
-    const int key0 = key_of(j);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BC) * RB);
+    const int key0 = j * BT;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)key0 * RB, min(N - key0, BT) * RB);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) dma16_buf<0>(r, off[i], st + (wid * IPW + i) * 1024);
   };
@@ -498,7 +516,7 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
     bf16x8 pk[NKB][2];
     float ts;
     if (j + 1 < n_tiles) {
-      qk(knext, snext);
+      qk(knext + hoff, snext);
       ts = expo(scur, m_run, pk);
       // the K reads lead; then each MFMA is followed by its share of the VALU
       constexpr int NM = NKB * (D / 16);
@@ -522,17 +540,20 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb32][r]);
       mx = max_halves(mx);
       const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
+      // (SPLIT: an odd wave's rows may have seen no key yet; they keep
+      // m = -inf, l = 0, O = 0 and take their exponentials against 0)
+      const bool none = SPLIT && m_new == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      ts = expo(scur, m_run, pk);
+      ts = expo(scur, none ? 0.f : m_run, pk);
     }
     l_run += ts;
-    pv(vcur, pk);
+    pv(vcur + hoff, pk);
   };
 
   f32x16 sa[NKB], sb[NKB];
@@ -541,12 +562,39 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
   if (n_tiles > 1) issue(kg, dma_k, 1, ks1);
   wait_vmem();
   barrier_lds();
-  qk(ks0, sa);
+  qk(ks0 + hoff, sa);
   for (int j = 0; j < n_tiles; j += 2) {
     step(j, sa, sb, ks1, vs0, ks0, vs1);
     if (j + 1 < n_tiles) step(j + 1, sb, sa, ks0, vs1, ks1, vs0);
   }
 
+  if constexpr (SPLIT) {
+    // odd waves -> LDS (in their own register order, so each lane of the
+    // partner reads back exactly its own row and columns) -> even waves merge
+    constexpr int NV = (D / 32) * 16 + 2;   // floats per lane
+    static_assert(64 * NV * 4 <= C::TILE, "a row block's merge area must fit one stage");
+    float* xbuf = (float*)(rb ? ks1 : ks0);   // each row block its own area (whole stages)
+    barrier_lds();                            // every wave done with the stages
+    if (par == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xbuf[(db * 16 + r) * 64 + lane] = o[db][r];
+      xbuf[(NV - 2) * 64 + lane] = m_run;
+      xbuf[(NV - 1) * 64 + lane] = l_run;
+    }
+    barrier_lds();
+    if (par == 1) return;
+    const float m1 = xbuf[(NV - 2) * 64 + lane], l1 = xbuf[(NV - 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);                 // finite: every row sees key 0 (causal) or N keys
+    const float a0 = fast_exp2(m_run - mm), a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xbuf[(db * 16 + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mm;
+  }
   const float l_tot = sum_halves(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -564,10 +612,10 @@ __device__ __forceinline__ void fwd_bf16_sp_item(const FwdParams& p, const WorkI
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_sp_kernel(FwdParams p) {
-  fwd_bf16_sp_item<D, CAUSAL>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
+  fwd_bf16_sp_item<D, CAUSAL, SPLIT>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
 }
 
 // =================================================== bf16, ping-pong =====
@@ -980,8 +1028,13 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
   const float* ksc = p.ks + (size_t)bkv * nsb;
   const float* vsc = p.vs + (size_t)bkv * nsb;
 
-  const int dma_k0 = dma_base<RB8, kSwzK>(wid * IPD, lane);   // K rows swizzled for the fragment reads
-  const int dma_r0 = wid * 1024 + lane * 16;                   // raw V: a plain copy
+  // Copies: with every wave issuing, wave w copies KB w of a tile; with
+  // group 0 alone (kFp8Plan 1 and 2), wave w copies KBs 2w and 2w + 1.
+  constexpr bool G0_DMA = kFp8Plan != 3;
+  constexpr int NDMA = G0_DMA ? 2 : 1;
+  const int dmw = G0_DMA ? 2 * (wid & 3) : wid;                // first KB this wave copies
+  const int dma_k0 = dma_base<RB8, kSwzK>(dmw, lane);          // K rows swizzled for the fragment reads
+  const int dma_r0 = dmw * 1024 + lane * 16;                   // raw V: a plain copy
   int koff[D / 64][2];   // K fragment: row lr, 16-byte units 4 kb + 2 g and + 1
 #pragma unroll
   for (int kb = 0; kb < D / 64; ++kb)
@@ -994,8 +1047,11 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
 #pragma unroll
   for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RBV + v_swz<RBV>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
-  // decode: this thread's 16 fp8 values (row tid / 8, columns 16 (tid % 8) ..)
-  const int drow = tid >> 3, du = tid & 7;
+  // decode: this thread's 16 fp8 values (row dt / 8, columns 16 (dt % 8) ..),
+  // and with one group decoding also those of row dt / 8 + 32
+  constexpr bool DEC1 = kFp8Plan != 3;
+  const int dt = DEC1 ? (tid & 255) : tid;
+  const int drow = dt >> 3, du = dt & 7;
   const int dst0 = drow * RBV + v_swz<RBV>(drow, 2 * du) * 16;
   const int dst1 = drow * RBV + v_swz<RBV>(drow, 2 * du + 1) * 16;
 
@@ -1009,25 +1065,32 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
   auto issue_k = [&](int j, unsigned char* st) {
     const int key0 = j * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kg + (size_t)key0 * D, min(N - key0, BC) * D);
-    dma16_buf<0>(r, dma_off<RB8, kSwzK>(dma_k0, 0), st + wid * 1024);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) dma16_buf<0>(r, dma_off<RB8, kSwzK>(dma_k0, i), st + (dmw + i) * 1024);
   };
   auto issue_r = [&](int j, unsigned char* st) {
     const int key0 = j * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vg + (size_t)key0 * D, min(N - key0, BC) * D);
-    dma16_buf<0>(r, dma_r0, st + wid * 1024);
-  };
-  auto decode = [&](const unsigned char* rl, unsigned char* vl) {
-    const i32x4 x = *(const i32x4*)(rl + tid * 16);
-    i32x4 lo, hi;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      lo[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, false));
-      lo[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, true));
-      hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, false));
-      hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, true));
+    for (int i = 0; i < NDMA; ++i) dma16_buf<0>(r, dma_r0 + i * 1024, st + (dmw + i) * 1024);
+  };
+  // (the swizzle of a bf16 V row depends on its row mod 4, so row r + 32
+  // sits 32 rows after row r)
+  auto decode = [&](const unsigned char* rl, unsigned char* vl) {
+#pragma unroll
+    for (int part = 0; part < (DEC1 ? 2 : 1); ++part) {
+      const i32x4 x = *(const i32x4*)(rl + (dt + 256 * part) * 16);
+      i32x4 lo, hi;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        lo[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, false));
+        lo[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, true));
+        hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, false));
+        hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, true));
+      }
+      *(i32x4*)(vl + dst0 + part * 32 * RBV) = lo;
+      *(i32x4*)(vl + dst1 + part * 32 * RBV) = hi;
     }
-    *(i32x4*)(vl + dst0) = lo;
-    *(i32x4*)(vl + dst1) = hi;
   };
   auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {
     const int key0 = j * BC;
@@ -1135,22 +1198,26 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
       }
   };
 
-  // Phase j: K_j in k[j & 1]; the raw V_j in r[j & 1] (loaded in phase j),
-  // decoded in phase j + 1 into v[j & 1] and used there.
+  // Phase j: K_j in k[j & 1]; the raw V_j in r[j & 1], loaded in phase j - 1;
+  // V_j decoded in phase j into v[j & 1] and used in phase j + 1, whose
+  // opening barrier makes it visible: one barrier per phase.
   bool has_s = false, has_p = false;
   auto step = [&](int j, const unsigned char* kc, unsigned char* kn, unsigned char* r_load,
-                  const unsigned char* r_dec, unsigned char* v_dec) __attribute__((always_inline)) {
+                  const unsigned char* r_dec, unsigned char* v_dec, const unsigned char* v_use)
+      __attribute__((always_inline)) {
     wait_vmem();
-    barrier_lds();   // K_j and raw V_{j-1} landed; the stages overwritten below are free
-    if (j + 1 < n_tiles) issue_k(j + 1, kn);
-    if (j < n_tiles) issue_r(j, r_load);
-    if (j >= 1) decode(r_dec, v_dec);
-    barrier_lds();   // decoded V_{j-1} visible to every wave
+    barrier_lds();   // K_j, raw V_j and decoded V_{j-1} in place; the stages written below are free
+    if (!G0_DMA || grp == 0) {
+      if (j + 1 < n_tiles) issue_k(j + 1, kn);
+      if (j + 1 < n_tiles) issue_r(j + 1, r_load);
+    }
+    if (kFp8Plan != 1 && (!DEC1 || grp == 0) && j < n_tiles) decode(r_dec, v_dec);
     if (grp == 1 && has_s) {
       softmax(j - 1);
       has_p = true;
     }
-    if (has_p) pv(v_dec);
+    if (kFp8Plan == 1 && grp == 1 && j < n_tiles) decode(r_dec, v_dec);
+    if (has_p) pv(v_use);
     has_p = false;
     has_s = j < n_tiles && qk(j, kc);
     if (grp == 0 && has_s) {
@@ -1159,10 +1226,13 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
       has_s = false;
     }
   };
-  issue_k(0, k0);
+  if (!G0_DMA || grp == 0) {
+    issue_k(0, k0);
+    issue_r(0, r0);
+  }
   for (int j = 0; j <= n_tiles; j += 2) {
-    step(j, k0, k1, r0, r1, v1);
-    if (j + 1 <= n_tiles) step(j + 1, k1, k0, r1, r0, v0);
+    step(j, k0, k1, r1, r0, v0, v1);
+    if (j + 1 <= n_tiles) step(j + 1, k1, k0, r0, r1, v1, v0);
   }
 
   const float l_tot = sum_halves(l_run);
@@ -1805,10 +1875,16 @@ static hipError_t launch_bf16(FwdParams& p, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_sp(FwdParams& p, hipStream_t s) {
-  // one workgroup per item (two resident per CU)
+  // One workgroup per item (two resident per CU).  When the 128-row items
+  // would all be resident at once, the split instance with 64-row items
+  // (waves splitting the keys) halves the longest item.
   using C = Bf16Cfg<D, 4, 64, 2>;
+  if ((long long)p.B * p.H * ((p.N + C::BR - 1) / C::BR) <= 2LL * cu_count()) {
+    finish_grid(p, 64);
+    return launch_kernel(fwd_bf16_sp_kernel<D, CAUSAL, true>, dim3(p.total), dim3(C::NT), s, p);
+  }
   finish_grid(p, C::BR);
-  return launch_kernel(fwd_bf16_sp_kernel<D, CAUSAL>, dim3(p.total), dim3(C::NT), s, p);
+  return launch_kernel(fwd_bf16_sp_kernel<D, CAUSAL, false>, dim3(p.total), dim3(C::NT), s, p);
 }
 
 template <int D, bool CAUSAL>

@@ -85,11 +85,10 @@ def test_blocksparse_all_on_matches_fa_fwd(d, causal):
     o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
     o2, l2 = fa.fa_fwd_blocksparse(q, k, v, torch.ones(4, 3, 3, dtype=torch.uint8, device=DEV), causal=causal)
     torch.cuda.synchronize()
-    if d == 64 and causal:      # the same kernel serves both calls: bit-exact
-        assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    else:                       # another tiling: the same values up to rounding
-        assert float((o1.float() - o2.float()).abs().max()) <= TOL
-        assert float((l1 - l2).abs().max()) <= TOL
+    # another tiling (short causal d=64 grids split each row's keys over two
+    # waves in the plain forward): the same values up to rounding
+    assert float((o1.float() - o2.float()).abs().max()) <= TOL
+    assert float((l1 - l2).abs().max()) <= TOL
 
 
 BWD_CASES = [

@@ -93,14 +93,22 @@ def test_masked_small(case):
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_masked_without_mask_matches_fa_fwd(d, causal):
     """Full-length sequences and no window through the masked kernels give
-    exactly what the plain forward gives."""
+    what the plain forward gives: bit for bit where both run the same
+    schedule.  For short causal d=64 grids the plain forward splits each
+    row's keys over two waves and merges the halves (another tiling, whose
+    waves round P to bf16 against their own running maxima), so there the two
+    agree up to rounding, within the stated tolerance."""
     w = syn.Workload("m", 2, 4, 2, 333, d, "bf16", causal, 1.0, 40 + d)
     x = syn.make_inputs(w)
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
     o2, l2 = fa.fa_fwd_masked(q, k, v, torch.full((2,), 333, dtype=torch.int32, device=DEV), None, causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if d == 64 and causal:
+        assert float((o1.float() - o2.float()).abs().max()) <= TOL
+        assert float((l1 - l2).abs().max()) <= TOL
+    else:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_masked_unsupported_dtypes_raise():
