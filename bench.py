@@ -80,6 +80,13 @@ def parse():
     ap.add_argument("--check-trace", default=None, metavar="CSV",
                     help="check a rocprofv3 kernel_stats.csv of a bench run (with --only W, or the "
                          "headline) against the library's kernel names and exit")
+    ap.add_argument("--summary-out", default=None, metavar="MD",
+                    help="with --check-trace: also write the trace summary (markdown) here")
+    ap.add_argument("--summary-cmd", default="", help="the command that produced the trace (for the summary)")
+    ap.add_argument("--traffic", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv of a --only W run "
+                         "and of a --copy-probe run: write W's HBM bytes per launch into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -267,9 +274,9 @@ LIB_KERNELS = ("fwd_bf16_kernel", "fwd_bf16_sp_kernel", "fwd_bf16_pp_kernel", "f
 DOMINANT = {"C5": "fa::fwd_fp8_pp_kernel<128, true", "Ta": "fa::fwd_bf16_pp_kernel<128, true",
             "Ta_gqa": "fa::fwd_bf16_pp_kernel<128, true", "Tb": "fa::fwd_bf16_pp_kernel<128, true",
             "Tc": "fa::fwd_bf16_pp_kernel<128, true", "C3": "fa::fwd_bf16_pp_kernel<128, true",
-            "C2a": "fa::fwd_bf16_sp_kernel<64, true>", "C2a_nc": "fa::fwd_bf16_pp_kernel<64, false",
+            "C2a": "fa::fwd_bf16_sp_kernel<64, true, true>", "C2a_nc": "fa::fwd_bf16_pp_kernel<64, false",
             "C2b": "fa::fwd_bf16_pairs_kernel<256, true", "C1": "fa::fwd_f32_kernel<64, true",
-            "C4": "fa::fwd_bf16_sp_kernel<64, true>"}
+            "C4": "fa::fwd_bf16_sp_kernel<64, true, false>"}
 HEADLINE_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fp8_d128_causal_C5.md")
 
 
@@ -392,9 +399,10 @@ def base_name(kernel):
 
 
 def check_kernels(rows, workload):
-    """The trace's kernels by time: every fa:: kernel must be one of the
-    library's, and the dominant one the kernel the instance table picks for
-    the workload.  Returns a dict with ok and the reasons."""
+    """The trace's kernels: every fa:: kernel must be one of the library's,
+    and the forward kernel with the most time must be the one the instance
+    table picks for the workload (a run with the backward also shows its
+    kernels).  Returns a dict with ok and the reasons."""
     want = DOMINANT.get(workload)
     ours = [r for r in rows if "fa::" in r[0]]
     problems = []
@@ -403,9 +411,10 @@ def check_kernels(rows, workload):
     for r in ours:
         if base_name(r[0]) not in LIB_KERNELS:
             problems.append(f"unknown kernel {r[0]}")
-    top = max(ours, key=lambda r: r[1] * r[2]) if ours else None
+    fwd = [r for r in ours if base_name(r[0]).startswith(("fwd_", "kv_"))] or ours
+    top = max(fwd, key=lambda r: r[1] * r[2]) if fwd else None
     if want and top and want not in top[0]:
-        problems.append(f"dominant kernel {top[0]} is not {want}")
+        problems.append(f"dominant forward kernel {top[0]} is not {want}")
     return {"ok": not problems, "expected": want, "dominant": top[0] if top else None,
             "dominant_avg_us": top[2] if top else None, "problems": problems}
 
@@ -420,13 +429,102 @@ def parse_kernel_stats(path):
     return rows
 
 
+def write_summary(rows, path, workload, cmd):
+    """Markdown summary of a kernel trace: per kernel, calls and durations."""
+    import synthetic as syn
+    tot = sum(c * a for _, c, a in rows) or 1.0
+    w = syn.WORKLOADS.get(workload) or syn.KV_WORKLOADS.get(workload) or \
+        syn.MASKED_WORKLOADS.get(workload) or syn.BLOCKSPARSE_WORKLOADS.get(workload)
+    what = (f"B={w.B}, H={w.H}, H_kv={w.H_kv}, N={getattr(w, 'N', None) or getattr(w, 'N_kv', None)}, "
+            f"d={w.d}, {w.dtype}, {'causal' if w.causal else 'non-causal'}")
+    lines = [f"# Kernel trace: {workload} ({what})", "",
+             f"command (from the repository root): {cmd}", "",
+             "| kernel | calls | average (us) | share of kernel time |", "|---|---|---|---|"]
+    for name, calls, avg in sorted(rows, key=lambda r: -r[1] * r[2]):
+        lines.append(f"| `{name}` | {calls} | {avg:.1f} | {100.0 * calls * avg / tot:.1f}% |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def counter_rows(path):
+    """(kernel, counter value) per dispatch of a rocprofv3 counter_collection.csv."""
+    import csv
+    with open(path, newline="") as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
+
+
+def compulsory_bytes(w):
+    """Bytes a forward must move at least: Q, K, V (and fp8 scales) read once, O and LSE written once."""
+    elt = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    q = w.B * w.H * w.N * w.d * elt
+    kv = 2 * w.B * w.H_kv * w.N * w.d * elt
+    sc = 0 if w.dtype != "fp8" else 4 * ((w.N + 127) // 128) * (w.B * w.H + 2 * w.B * w.H_kv)
+    out = w.B * w.H * w.N * w.d * (4 if w.dtype == "f32" else 2) + 4 * w.B * w.H * w.N
+    return q + kv + sc, out
+
+
+def traffic_entry(args):
+    """HBM bytes per launch of a workload's dominant kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain 1 GiB device copy (which reads and writes 2^30 bytes)."""
+    fetch, write, cfetch, cwrite = (counter_rows(p) for p in args.traffic)
+    w = syn_workload(args.only)
+    want = DOMINANT[args.only]
+    avg = lambda rows: sum(v for k, v in rows if want in k) / max(1, sum(1 for k, _ in rows if want in k))
+    cavg = lambda rows: sum(v for k, v in rows if "copyBuffer" in k) / max(1, sum(1 for k, _ in rows if "copyBuffer" in k))
+    ff, wf = (1 << 30) / (cavg(cfetch) * 1024), (1 << 30) / (cavg(cwrite) * 1024)
+    rd, wr = avg(fetch) * 1024 * ff, avg(write) * 1024 * wf
+    comp_r, comp_w = compulsory_bytes(w)
+    return {"workload": args.only, "kernel": want, "fetch_kib": avg(fetch), "write_kib": avg(write),
+            "fetch_factor": ff, "write_factor": wf, "read_bytes": rd, "write_bytes": wr,
+            "bytes_per_launch": rd + wr, "compulsory_read_bytes": comp_r, "compulsory_write_bytes": comp_w,
+            "read_over_compulsory": rd / comp_r}
+
+
 def main():
     args = parse()
     if args.check_trace:
         rows = parse_kernel_stats(args.check_trace)
         res = check_kernels(rows, args.only or HEADLINE)
+        if args.summary_out:
+            write_summary(rows, args.summary_out, args.only or HEADLINE, args.summary_cmd)
         print(json.dumps({"trace": args.check_trace, "workload": args.only or HEADLINE, **res}))
         sys.exit(0 if res["ok"] else 1)
+    if args.traffic:
+        ent = traffic_entry(args)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            t = {}
+        if t.get("source_hash") != source_hash():
+            t = {"source_hash": source_hash(), "kernels": {}}
+        t["kernels"][kernel_name(syn_workload(args.only))] = ent
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        if args.summary_out:
+            mib = 1 << 20
+            with open(args.summary_out, "w") as f:
+                f.write(f"# HBM traffic per launch: {args.only}, `{ent['kernel']}...>`\n\n"
+                        f"commands (from the repository root), one counter per run:\n\n"
+                        f"    rocprofv3 --pmc FETCH_SIZE -d <dir> -o c --output-format csv -- python3 bench.py "
+                        f"--only {args.only} --steps 2 --warmup 0 --no-cpu-baseline --no-extra\n"
+                        f"    rocprofv3 --pmc WRITE_SIZE (the same program)\n"
+                        f"    rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE -- python3 bench.py --copy-probe\n"
+                        f"    python3 bench.py --only {args.only} --traffic <fetch csv> <write csv> <copy fetch csv> "
+                        f"<copy write csv> --summary-out <this file>\n\n"
+                        f"Calibration: a 1 GiB device copy reads 2^30 and writes 2^30 bytes; its FETCH_SIZE reads "
+                        f"{(1 << 30) / ent['fetch_factor'] / 1024:.0f} KiB and its WRITE_SIZE "
+                        f"{(1 << 30) / ent['write_factor'] / 1024:.0f} KiB per dispatch, so bytes = FETCH_SIZE x 1024 x "
+                        f"{ent['fetch_factor']:.4f} and WRITE_SIZE x 1024 x {ent['write_factor']:.4f}.\n\n"
+                        f"| FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM read (MiB) | HBM write (MiB) | compulsory read (MiB) "
+                        f"| compulsory write (MiB) | read / compulsory |\n|---|---|---|---|---|---|---|\n"
+                        f"| {ent['fetch_kib']:.0f} | {ent['write_kib']:.0f} | {ent['read_bytes'] / mib:.1f} | "
+                        f"{ent['write_bytes'] / mib:.1f} | {ent['compulsory_read_bytes'] / mib:.1f} | "
+                        f"{ent['compulsory_write_bytes'] / mib:.1f} | {ent['read_over_compulsory']:.2f} |\n\n"
+                        f"Kernel sources hash (bench.py source_hash): {source_hash()}\n")
+        print(json.dumps(ent))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
