@@ -95,10 +95,8 @@ def kernel_resources(obj: str) -> list[dict]:
     return out
 
 
-# Kernels allowed to use scratch, measured faster than the spill-free
-# alternative: the d = 128 dK/dV backward spills a few registers at two waves
-# a SIMD (faster than one wave a SIMD).
-SCRATCH_ALLOWED = ("bwd_dkdv_kernelILi128E",)
+# Kernels allowed to use scratch: none.
+SCRATCH_ALLOWED = ()
 
 
 def check_no_scratch(objs) -> None:

@@ -190,7 +190,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     dv[i] = f32x16{};
   }
 
-  const int dma0 = dma_base<RB, kSwzRt>(wid * IPW, lane);
+  const int dma0_ = dma_base<RB, kSwzRt>(wid * IPW, lane);
   // LDS read offsets of block 0 (the others are formed per tile, below)
   const int roff0 = lr * RB + rt_swz<RB>(lr, g) * 16;
   const int troff0 = tr_off<RB>(lane, 0, 0);
@@ -249,6 +249,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto issue = [&](int it_idx, unsigned char* st) {
     int gi, qt;
     step_tile(it_idx, gi, qt);
+    const int dma0 = D == 128 ? dma_base<RB, kSwzRt>(wid * IPW,
+                                                      __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)))
+                              : dma0_;
     const size_t bh = (size_t)b * p.H + kvh * G + gi;
     const int row0 = qt * BQ;
     const int rows = min(L - row0, BQ);          // rows past the valid ones read as zero
@@ -276,7 +279,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     // and column block db's, are block 0's XOR a constant (the swizzle is
     // XOR-linear in bits no lane bit shares, as for the DMA copies); made
     // opaque once per tile so they are formed here instead of kept live.
+    // (at d = 128 the bases are formed from the lane id per tile: three
+    // registers fewer across the loop, which kept the kernel from spilling)
     int rb0 = roff0, tb0 = troff0;
+    if constexpr (D == 128) {
+      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      rb0 = (ln & 31) * RB + rt_swz<RB>(ln & 31, ln >> 5) * 16;
+      tb0 = tr_off<RB>(ln, 0, 0);
+    }
     asm volatile("" : "+v"(rb0), "+v"(tb0));
     auto RO = [&](int kb) { return rb0 ^ (rt_swz<RB>(0, 2 * kb) * 16); };
     auto TO = [&](int sec, int db) { return (tb0 ^ (rt_swz<RB>(8 * sec, db * 4) * 16)) + sec * 8 * RB; };
@@ -417,11 +427,15 @@ void bwd_dkdv_kernel(BwdParams p) {
     bf16* dkr = (bf16*)p.dk + ((size_t)bkv * N + mykey) * D;
     bf16* dvr = (bf16*)p.dv + ((size_t)bkv * N + mykey) * D;
     const float sc = p.scale;
+    // (the lane's half, formed again from the lane id in the unmasked
+    // instances: kept live across the loop it was the one register the causal
+    // d = 128 instance spilled)
+    const int g_e = MASK ? g : __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int col = db * 32 + 8 * a + 4 * g;
+        const int col = db * 32 + 8 * a + 4 * g_e;
         *(i32x2*)(dkr + col) = i32x2{(int)pack_bf16(dk[db][4 * a] * sc, dk[db][4 * a + 1] * sc),
                                      (int)pack_bf16(dk[db][4 * a + 2] * sc, dk[db][4 * a + 3] * sc)};
         *(i32x2*)(dvr + col) = i32x2{(int)pack_bf16(dv[db][4 * a], dv[db][4 * a + 1]),
