@@ -649,16 +649,38 @@ struct PpCfg {
 // MASK, sequence b is valid for its first len_b rows (p.seqlens) and, with a
 // window w >= 0, query i sees only keys i - w .. i (see mask_of).  (Block
 // masks go to the four-wave kernel, whose workgroup is one query block.)
-template <int D, bool CAUSAL, int BC_, bool LATE, bool MASK>
-__device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
+//
+// On the looping grid (NEXT) the item's Q reaches the waves through LDS: each
+// wave copies its own 32 rows by LDS DMA into its own part of a Q stage and
+// reads its fragments from there, so no other wave touches them.  Right
+// after an item's closing phase (where no K stage is read any more) each wave
+// copies its rows of the next item's Q and its share of that item's first K
+// tile, and the epilogue's stores overlap those copies, so the next item
+// starts with its operands in LDS or on their way.  `nx` is the next item
+// (bh < 0: none); `pre` says whether this item's Q and first K tile were
+// copied so.
+template <int D, bool CAUSAL, int BC_, bool LATE, bool MASK, bool NEXT>
+__device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi, const WorkItem nx, bool pre) {
   using C = PpCfg<D, BC_, LATE>;
   constexpr int BR = C::BR, BC = C::BC, RB = C::RB, IPD = C::IPD, NKB = C::NKB, NST = C::NST;
+  static_assert(!NEXT || (!LATE && !MASK && RB == 256), "next-item copies only on the plain d = 128 schedule");
+  constexpr int QPW = BR * RB / 1024 / C::NW;    // 1 KB copies of one wave's Q rows
   __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char k2[NST > 2 ? C::TILE : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v2[NST > 2 ? C::TILE : 1];
+  // Per-wave regions for NEXT: Q rows (32 x RB bytes) and the epilogue's O
+  // staging (16 rows).  Being smaller than the K/V stages they are placed
+  // after them, so the stages read every phase keep LDS addresses below
+  // 64 KB, within reach of the read instructions' immediate offsets (one
+  // 64 KB array would go first and cost an address add per read).
+  constexpr int QW = NEXT ? 32 * RB : 1, OW = NEXT ? 16 * RB : 1;
+  __shared__ __attribute__((aligned(1024))) unsigned char qs0[QW], qs1[QW], qs2[QW], qs3[QW];
+  __shared__ __attribute__((aligned(1024))) unsigned char qs4[QW], qs5[QW], qs6[QW], qs7[QW];
+  __shared__ __attribute__((aligned(1024))) unsigned char os0[OW], os1[OW], os2[OW], os3[OW];
+  __shared__ __attribute__((aligned(1024))) unsigned char os4[OW], os5[OW], os6[OW], os7[OW];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -684,13 +706,6 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
   const int n_tiles = (kv_end + BC - 1) / BC - t0;   // tiles j = 0.. stand for t0 + j
   auto tile_of = [&](int j) -> int { return t0 + j; };
 
-  bf16x8 qr[D / 16];
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) {
-    bf16x8 x = {};
-    if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
-    qr[kb] = x;
-  }
   const int dwid = wid & (C::DW - 1);   // this wave's share of a DMA'd tile
   int dma_k[IPD], dma_v[IPD];
 #pragma unroll
@@ -712,6 +727,49 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
 #pragma unroll
   for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RB + v_swz<RB>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+
+  // Copies for NEXT: the wave's 32 rows of an item's Q, swizzled as a K tile
+  // (so its fragments are read as K's are: row lr, units 2 kb + g), and the
+  // wave's share of an item's first K tile (no mask: keys 0 .. BC - 1).
+  unsigned char* const qw = wid == 0 ? qs0 : wid == 1 ? qs1 : wid == 2 ? qs2 : wid == 3 ? qs3
+                         : wid == 4 ? qs4 : wid == 5 ? qs5 : wid == 6 ? qs6 : qs7;
+  unsigned char* const ow = wid == 0 ? os0 : wid == 1 ? os1 : wid == 2 ? os2 : wid == 3 ? os3
+                         : wid == 4 ? os4 : wid == 5 ? os5 : wid == 6 ? os6 : os7;
+  auto issue_q = [&](const WorkItem& it) {
+    const int qf = it.qt * BR + wid * 32;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc((const unsigned char*)p.q + ((size_t)it.bh * N + qf) * RB, max(min(N - qf, 32), 0) * RB);
+    const int base = dma_base<RB, kSwzK>(wid * QPW, lane) - wid * QPW * 1024;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+      dma16_buf<0>(r, dma_off<RB, kSwzK>(base, i), qw + i * 1024);
+  };
+  auto issue_k0 = [&](const WorkItem& it) {
+    const int bi = it.bh / p.H, hi = it.bh - bi * p.H;
+    const size_t kv = (size_t)(bi * p.H_kv + hi / (p.H / p.H_kv)) * N * RB;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const unsigned char*)p.k + kv, min(N, BC) * RB);
+#pragma unroll
+    for (int i = 0; i < IPD; ++i) dma16_buf<0>(r, dma_k[i], k0 + (dwid * IPD + i) * 1024);
+  };
+  const bool has_nx = NEXT && nx.bh >= 0;
+  bf16x8 qr[D / 16];
+  if constexpr (NEXT) {
+    if (!pre) {
+      issue_q(wi);
+      issue_k0(wi);
+    }
+    wait_vmem();   // this wave's Q rows (its own copies) are in LDS
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      qr[kb] = *(const bf16x8*)(qw + (kb / NKO) * 256 + koff[kb % NKO]);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      bf16x8 x = {};
+      if (myq < N) x = *(const bf16x8*)(qg + (size_t)myq * RB + (kb * 16 + 8 * g) * 2);
+      qr[kb] = x;
+    }
+  }
 
   const float c = p.scale_log2;
   f32x16 o[D / 32];
@@ -927,15 +985,53 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
       has_s = false;
     }
   };
-  issue_one(kg, dma_k, 0, k0);
+  if (!NEXT) issue_one(kg, dma_k, 0, k0);
   for (int j = 0; j <= n_tiles; j += 2) {
     step(j, k0, v1, k1, v0);
     if (j + 1 <= n_tiles) step(j + 1, k1, v0, k0, v1);
   }
+  // The next item's copies go out before this item's epilogue, whose stores
+  // they then overlap: the wave's Q rows, and K_0 into K stage 0, which no
+  // wave reads after the closing phase's barrier.
+  if (has_nx) {
+    issue_q(nx);
+    issue_k0(nx);
+  }
   }
 
   const float l_tot = sum_halves(l_run);
-  if (MASK && (myq >= L || l_tot == 0.f)) {   // padding, or a row that sees no key
+  if constexpr (NEXT) {
+    // O through the wave's 16-row staging region, two rounds of 16 rows: a
+    // lane holds 8-byte pieces of its row, which as global stores would touch
+    // 32 rows per instruction; staged, each store writes 1 KB of whole rows.
+    // (16-byte unit u of staged row r sits at unit u ^ r: conflict-free
+    // 8-byte writes down a column and 16-byte reads along rows.)
+    const float inv = 1.f / l_tot;
+    unsigned char* const og = (unsigned char*)p.o + ((size_t)wi.bh * N + q0) * RB;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      if ((lr >> 4) == rd) {
+        const int row = lr & 15;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const uint32_t lo = pack_bf16(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+            const uint32_t hi = pack_bf16(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+            *(i32x2*)(ow + row * RB + (((db * 4 + a) ^ row) << 4) + 8 * g) = i32x2{(int)lo, (int)hi};
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 16 * RB / 1024; ++k) {
+        const int row = k * (1024 / RB) + (lane >> 4), u = lane & 15;
+        const i32x4 val = *(const i32x4*)(ow + row * RB + ((u ^ row) << 4));
+        if (q0 + 16 * rd + row < N) *(i32x4*)(og + (16 * rd + row) * RB + u * 16) = val;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    if (p.lse && g == 0 && myq < N) p.lse[(size_t)wi.bh * N + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  } else if (MASK && (myq >= L || l_tot == 0.f)) {   // padding, or a row that sees no key
     write_empty_rows(p, wi.bh, myq, g, D);
   } else if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -956,20 +1052,27 @@ __device__ __forceinline__ void pp_item(const FwdParams& p, const WorkItem wi) {
 // With PERSIST, one workgroup per CU loops over its share of the items (see
 // persistent_map); otherwise one workgroup per item.  Between items the
 // workgroup synchronises: an item's first DMAs must not land in a stage a
-// slower wave is still reading for the previous item.
+// slower wave is still reading for the previous item.  With the next-item
+// copies (NEXT) no such sync is needed: they go to stages nobody reads by then
+// (the wave's own Q rows; K stage 0 after the closing phase's barrier), and
+// an item's first tile copies follow its first phase's barrier.
 template <int D, bool CAUSAL, int BC_, bool LATE, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_pp_kernel(FwdParams p) {
   if constexpr (PERSIST) {
+    constexpr bool NEXT = !LATE && !MASK;
     const PersistentMap pm = persistent_map(blockIdx.x, gridDim.x, p.total, p.remap, p.group_items);
-    for (int r = 0;; ++r) {
-      const int w = persistent_item(pm, r);
-      if (w < 0) break;
-      if (r > 0) __syncthreads();
-      pp_item<D, CAUSAL, BC_, LATE, MASK>(p, item_of(w, p.n_qt));
+    int w = persistent_item(pm, 0);
+    for (int r = 0; w >= 0; ++r) {
+      const int wn = persistent_item(pm, r + 1);
+      if (!NEXT && r > 0) __syncthreads();
+      pp_item<D, CAUSAL, BC_, LATE, MASK, NEXT>(p, item_of(w, p.n_qt),
+                                              wn >= 0 ? item_of(wn, p.n_qt) : WorkItem{-1, 0}, r > 0);
+      w = wn;
     }
   } else {
-    pp_item<D, CAUSAL, BC_, LATE, MASK>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items));
+    pp_item<D, CAUSAL, BC_, LATE, MASK, false>(p, map_work(blockIdx.x, p.total, p.n_qt, p.remap, p.group_items),
+                                               WorkItem{-1, 0}, false);
   }
 }
 
