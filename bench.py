@@ -87,6 +87,9 @@ def parse():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv of a --only W run "
                          "and of a --copy-probe run: write W's HBM bytes per launch into profiles/traffic.json")
+    ap.add_argument("--counter-summary", nargs="+", default=None, metavar="W=DIR",
+                    help="summarise rocprofv3 --kernel-trace --pmc runs (one output directory per workload W, "
+                         "SQ/GRBM counters) into a markdown table (--summary-out) and exit")
     return ap.parse_args()
 
 
@@ -453,6 +456,97 @@ def counter_rows(path):
         return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
 
 
+SQ_PASS = ("SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+           "SQ_INSTS_VALU_TRANS_F32", "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE")
+LDS_PASS = ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES",
+            "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")
+N_SIMD, N_XCD = 1024, 8
+
+
+def counter_table(directory):
+    """Per kernel of one rocprofv3 --kernel-trace --pmc run (its output directory):
+    dispatches, median duration (us) and the median of each counter per dispatch."""
+    import csv
+    import glob
+    import statistics
+    cfiles = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    tfiles = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    dur = {}
+    for tf in tfiles:
+        with open(tf, newline="") as f:
+            for r in csv.DictReader(f):
+                dur[(tf, r["Dispatch_Id"])] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    per = {}
+    for cf in cfiles:
+        with open(cf, newline="") as f:
+            for r in csv.DictReader(f):
+                d = per.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for k, disp in per.items():
+        us = [v[1] for v in dur.values() if v[0] == k]
+        names = sorted({c for d in disp.values() for c in d})
+        out[k] = {"dispatches": len(disp), "us": statistics.median(us) if us else float("nan"),
+                  **{c: statistics.median([d.get(c, 0.0) for d in disp.values()]) for c in names}}
+    return out
+
+
+def counter_summary_rows(tables):
+    """Derived figures per (workload, kernel) from counter_table results."""
+    rows = []
+    for wname, tab in tables:
+        for k, c in sorted(tab.items(), key=lambda kv: -kv[1]["us"] * kv[1]["dispatches"]):
+            if not any(n in k for n in LIB_KERNELS):
+                continue
+            cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+            r = {"workload": wname, "kernel": k.replace("void ", "").split("(")[0], "us": c["us"],
+                 "clock_ghz": cyc / (c["us"] * 1e3) if c["us"] >= 20 and cyc else None}
+            if "SQ_INSTS_MFMA" in c and cyc:
+                mf = c["SQ_INSTS_MFMA"]
+                r.update(mfma_busy=c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc,
+                         coexec=c["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMD / cyc,
+                         mfma_insts=mf, valu_insts=c["SQ_INSTS_VALU"] - mf, exp_insts=c["SQ_INSTS_VALU_TRANS_F32"],
+                         trans_share=c["SQ_INSTS_VALU_TRANS_F32"] * 16 / N_SIMD / cyc)
+            if "SQ_INSTS_LDS" in c and cyc:
+                r.update(lds_insts=c["SQ_INSTS_LDS"],
+                         lds_conflict=c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_ACTIVE_INST_LDS"]),
+                         lds_wait=c["SQ_WAIT_INST_LDS"] / max(1.0, c["SQ_WAVE_CYCLES"]),
+                         any_wait=c["SQ_WAIT_ANY"] / max(1.0, c["SQ_WAVE_CYCLES"]))
+            rows.append(r)
+    return rows
+
+
+def write_counter_summary(rows, path, runs):
+    f3 = lambda v, fmt: "—" if v is None else fmt.format(v)
+    lines = ["# Matrix-pipe use, instruction mix and LDS waits per kernel (rocprofv3 counters)", "",
+             "commands (from the repository root), one run per workload W and counter pass:", "",
+             "    rocprofv3 --kernel-trace --pmc " + " ".join(SQ_PASS) + " -d <dir>/W -o c --output-format csv -- "
+             "python3 bench.py --only W --steps 2 --warmup 0 --no-cpu-baseline --no-extra [--with-bwd]",
+             "    rocprofv3 --kernel-trace --pmc " + " ".join(LDS_PASS) + " (the same program, some W)",
+             "    python3 bench.py --counter-summary " + " ".join(runs) + " --summary-out <this file>", "",
+             "How the columns are formed: kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); "
+             "clock = kernel cycles / duration (not shown under 20 us); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "1024 SIMDs / kernel cycles; co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / 1024 / kernel cycles; "
+             "instruction counts are totals over all waves (SQ_INSTS_VALU includes the MFMAs, subtracted here); "
+             "exp share = SQ_INSTS_VALU_TRANS_F32 x 16 cycles (a quarter-rate wave64 op) / 1024 / kernel cycles, "
+             "the fraction of every SIMD's time its transcendentals alone would take; LDS conflict = "
+             "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS; LDS wait and any wait = SQ_WAIT_INST_LDS and SQ_WAIT_ANY "
+             "over SQ_WAVE_CYCLES (per-wave fractions). Durations are medians of the counter runs' kernel "
+             "traces (collection slows kernels slightly).", "",
+             "| workload | kernel | us | clock (GHz) | MFMA busy | MFMA+VALU co-issue | MFMA insts | other VALU insts "
+             "| exp insts | exp share | LDS insts | LDS conflict | LDS wait | any wait |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['workload']} | `{r['kernel']}` | {r['us']:.1f} | {f3(r['clock_ghz'], '{:.2f}')} | "
+                     f"{f3(r.get('mfma_busy'), '{:.1%}')} | {f3(r.get('coexec'), '{:.1%}')} | "
+                     f"{f3(r.get('mfma_insts'), '{:.3g}')} | {f3(r.get('valu_insts'), '{:.3g}')} | "
+                     f"{f3(r.get('exp_insts'), '{:.3g}')} | {f3(r.get('trans_share'), '{:.1%}')} | "
+                     f"{f3(r.get('lds_insts'), '{:.3g}')} | {f3(r.get('lds_conflict'), '{:.1%}')} | "
+                     f"{f3(r.get('lds_wait'), '{:.1%}')} | {f3(r.get('any_wait'), '{:.1%}')} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def compulsory_bytes(w):
     """Bytes a forward must move at least: Q, K, V (and fp8 scales) read once, O and LSE written once."""
     elt = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
@@ -483,6 +577,18 @@ def traffic_entry(args):
 
 def main():
     args = parse()
+    if args.counter_summary:
+        tables = {}
+        for spec in args.counter_summary:          # several passes of one workload merge per kernel
+            wname, _, d = spec.partition("=")
+            for k, c in counter_table(d).items():
+                tables.setdefault(wname, {}).setdefault(k, {}).update({n: v for n, v in c.items()
+                                                                       if n not in tables[wname].get(k, {})})
+        rows = counter_summary_rows(list(tables.items()))
+        if args.summary_out:
+            write_counter_summary(rows, args.summary_out, args.counter_summary)
+        print(json.dumps(rows))
+        return
     if args.check_trace:
         rows = parse_kernel_stats(args.check_trace)
         res = check_kernels(rows, args.only or HEADLINE)

@@ -1150,13 +1150,17 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
 #pragma unroll
   for (int db = 0; db < NVO; ++db)
     voff[db] = vrow * RBV + v_swz<RBV>(vrow, db * 4 + 2 * (G & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
-  // decode: this thread's 16 fp8 values (row dt / 8, columns 16 (dt % 8) ..),
-  // and with one group decoding also those of row dt / 8 + 32
+  // decode: 8 fp8 values (16 bytes of bf16, one unit of a decoded row) at a
+  // time; 16 consecutive threads fill one row, so each 16-lane write covers 16
+  // distinct units (two rows per write group would meet in the same banks:
+  // the V swizzle never flips a unit's low bit)
   constexpr bool DEC1 = kFp8Plan != 3;
+  constexpr int DTH = DEC1 ? 256 : 512;                        // decoding threads
+  constexpr int UPR = RB8 / 8;                                 // 8-value pieces per row
   const int dt = DEC1 ? (tid & 255) : tid;
-  const int drow = dt >> 3, du = dt & 7;
-  const int dst0 = drow * RBV + v_swz<RBV>(drow, 2 * du) * 16;
-  const int dst1 = drow * RBV + v_swz<RBV>(drow, 2 * du + 1) * 16;
+  const int drow = dt / UPR, du = dt % UPR;
+  const int dst = drow * RBV + v_swz<RBV>(drow, du) * 16;     // rows DTH / UPR apart share the swizzle
+  static_assert((DTH / UPR) % 4 == 0, "the V swizzle repeats every 4 rows");
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -1177,22 +1181,16 @@ __device__ __forceinline__ void pp8_item(const FwdParams& p, const WorkItem wi) 
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) dma16_buf<0>(r, dma_r0 + i * 1024, st + (dmw + i) * 1024);
   };
-  // (the swizzle of a bf16 V row depends on its row mod 4, so row r + 32
-  // sits 32 rows after row r)
   auto decode = [&](const unsigned char* rl, unsigned char* vl) {
 #pragma unroll
-    for (int part = 0; part < (DEC1 ? 2 : 1); ++part) {
-      const i32x4 x = *(const i32x4*)(rl + (dt + 256 * part) * 16);
-      i32x4 lo, hi;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        lo[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, false));
-        lo[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.f, true));
-        hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, false));
-        hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[2 + w], 1.f, true));
-      }
-      *(i32x4*)(vl + dst0 + part * 32 * RBV) = lo;
-      *(i32x4*)(vl + dst1 + part * 32 * RBV) = hi;
+    for (int i = 0; i < T8 / 8 / DTH; ++i) {
+      const i32x2 x = *(const i32x2*)(rl + (dt + DTH * i) * 8);
+      i32x4 y;
+      y[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.f, false));
+      y[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.f, true));
+      y[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.f, false));
+      y[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.f, true));
+      *(i32x4*)(vl + dst + i * (DTH / UPR) * RBV) = y;
     }
   };
   auto qk = [&](int j, const unsigned char* kl) __attribute__((always_inline)) -> bool {

@@ -52,3 +52,33 @@ def test_profile_summaries_name_library_kernels(path):
     for name, _, _ in bench.read_summary(path):
         if "fa::" in name:
             assert bench.base_name(name) in bench.LIB_KERNELS, (path, name)
+
+
+def test_counter_summary_from_rocprof_csv(tmp_path):
+    """The counter summary joins a counter run's per-dispatch counters with its
+    kernel trace and forms the derived columns from the stated formulas."""
+    d = tmp_path / "W"
+    d.mkdir()
+    k = "void fa::fwd_fp8_pp_kernel<128, true, true>(fa::FwdParams)"
+    cnt = {"GRBM_GUI_ACTIVE": 8 * 2.0e6, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1024 * 2.0e6,
+           "SQ_VALU_MFMA_COEXEC_CYCLES": 0.25 * 1024 * 2.0e6, "SQ_INSTS_MFMA": 100.0, "SQ_INSTS_VALU": 700.0,
+           "SQ_INSTS_VALU_TRANS_F32": 0.1 * 1024 * 2.0e6 / 16}
+    with open(d / "c_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for disp in (1, 2):
+            for n, v in cnt.items():
+                f.write(f'{disp},"{k}",{n},{v / 2}\n{disp},"{k}",{n},{v / 2}\n')   # two partial rows a counter
+    with open(d / "c_kernel_trace.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        f.write(f'1,"{k}",1000,1001000\n2,"{k}",5000,1005000\n')
+    rows = bench.counter_summary_rows([("W", bench.counter_table(str(d)))])
+    assert len(rows) == 1
+    r = rows[0]
+    assert r["us"] == 1000.0 and abs(r["clock_ghz"] - 2.0) < 1e-12
+    assert abs(r["mfma_busy"] - 0.5) < 1e-12 and abs(r["coexec"] - 0.25) < 1e-12
+    assert r["valu_insts"] == 600.0 and abs(r["trans_share"] - 0.1) < 1e-12
+    out = tmp_path / "s.md"
+    bench.write_counter_summary(rows, str(out), ["W=" + str(d)])
+    text = out.read_text()
+    assert "| W | `fa::fwd_fp8_pp_kernel<128, true, true>` | 1000.0 | 2.00 | 50.0% | 25.0% |" in text
+    assert bench.read_summary(str(out)) == []
