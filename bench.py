@@ -20,9 +20,11 @@ The JSON line also carries:
                 cores, with both the causal-adjusted and the dense FLOP rate;
   kernel_check  the kernel names of the committed rocprofv3 trace summary of
                 the headline workload, checked against the library's kernels;
-  extra         the other workloads, each with its median (p10, p90) over
-                repetitions that each start with cold caches (a 512 MiB write
-                between repetitions flushes L2 and MALL): the causal bf16 d=128
+  extra         the other workloads, each with its median (p10, p90) over 20
+                repetitions after 3 warm-ups; short forwards and every backward
+                start each repetition with cold caches (a 512 MiB write between
+                repetitions flushes L2 and MALL), the long forwards (inputs
+                larger than MALL) run back to back: the causal bf16 d=128
                 forward at N >= 8192 (with the >= 50% target stated), the five
                 stated problems (fp32, bf16 d=64/256, GQA prefill, training
                 forward + backward), the backward at d=256 and GQA, padded /
@@ -50,6 +52,13 @@ TARGET_SHAPES = ["Ta", "Ta_gqa", "Tb", "Tc"]       # causal bf16, N >= 8192, d =
 TARGET_FRAC = 0.5                                  # of the dense bf16 MFMA peak
 EXTRA_FWD = TARGET_SHAPES + ["C1", "C2a", "C2a_nc", "C2b", "C3"]
 FLUSH_BYTES = 512 << 20                            # > the 256 MB MALL + 8 x 4 MB L2
+# Forward cases short enough (and with inputs small enough) for L2/MALL to
+# carry data from one repetition to the next: these, and every backward, are
+# timed with a 512 MiB write between repetitions.  The long forwards (the
+# T-shapes, C5, W1, S1: >= 1.9 ms over >= 384 MiB of inputs, more than MALL
+# holds) are timed back to back.
+SHORT_FWD = {"C1", "C2a", "C2a_nc", "C2b", "C3", "P1", "D1", "D1_ragged"}
+REPS, WARMUP = 20, 3                               # per extra workload and direction
 EXTRA_KV = ["D1", "D1_ragged"]
 EXTRA_MASKED = ["W1", "P1"]
 EXTRA_BLOCKSPARSE = ["S1"]
@@ -203,7 +212,7 @@ class MaskedCase:
         dq, dk, dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         fn = lambda: fa.fa_bwd_masked(self.q, self.k, self.v, self.o, self.lse, do, self.seqlens, self.w.window,
                                       causal=self.w.causal, scale=self.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
-        st = stats(time_launches(fn, reps=5, warmup=1, flush=True))
+        st = stats(time_launches(fn, reps=REPS, warmup=WARMUP, flush=True))
         tf = 2.5 * self.w.flops_fwd(self.lens) / (st["ms"] * 1e-3) / 1e12
         return {"kernel": f"bwd_bf16_d{self.w.d}_masked", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
@@ -247,7 +256,7 @@ class BlockSparseCase:
         fn = lambda: fa.fa_bwd_blocksparse(self.q, self.k, self.v, self.o, self.lse, do, self.bm,
                                            causal=self.w.causal, scale=self.scale, workspace=ws,
                                            dq=dq, dk=dk, dv=dv)
-        st = stats(time_launches(fn, reps=5, warmup=1, flush=True))
+        st = stats(time_launches(fn, reps=REPS, warmup=WARMUP, flush=True))
         tf = 2.5 * self.w.flops_fwd(self.bm_cpu) / (st["ms"] * 1e-3) / 1e12
         return {"kernel": f"bwd_bf16_d{self.w.d}_blocksparse", **st, "tflops": round(tf, 2),
                 "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
@@ -750,7 +759,7 @@ def main():
         for nm in EXTRA_FWD:
             log(f"extra: {nm}")
             c = Case(nm, dev)
-            s_ = stats(time_launches(c.fwd, reps=10, warmup=2, flush=True))
+            s_ = stats(time_launches(c.fwd, reps=REPS, warmup=WARMUP, flush=nm in SHORT_FWD))
             tf = c.w.flops_fwd() / (s_["ms"] * 1e-3) / 1e12
             extra[nm] = {"kernel": kernel_name(c.w), **s_, "tflops": round(tf, 2),
                          "frac_peak": round(tf / PEAK_TFLOPS[c.w.dtype], 4)}
@@ -763,7 +772,7 @@ def main():
         for nm in EXTRA_MASKED:
             log(f"extra: {nm}")
             c = MaskedCase(nm, dev)
-            extra[nm] = c.report(stats(time_launches(c.fwd, reps=10, warmup=2, flush=True)))
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=REPS, warmup=WARMUP, flush=nm in SHORT_FWD)))
             if nm == "W1":
                 extra[nm + ".bwd"] = c.bwd_report(dev)
             del c
@@ -771,21 +780,21 @@ def main():
         for nm in EXTRA_BLOCKSPARSE:
             log(f"extra: {nm}")
             c = BlockSparseCase(nm, dev)
-            extra[nm] = c.report(stats(time_launches(c.fwd, reps=10, warmup=2, flush=True)))
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=REPS, warmup=WARMUP, flush=nm in SHORT_FWD)))
             extra[nm]["bwd"] = c.bwd_report(dev)
             del c
             torch.cuda.empty_cache()
         for nm in EXTRA_KV:
             log(f"extra: {nm}")
             c = KvCase(nm, dev)
-            extra[nm] = c.report(stats(time_launches(c.fwd, reps=20, warmup=3, flush=True)))
+            extra[nm] = c.report(stats(time_launches(c.fwd, reps=REPS, warmup=WARMUP, flush=True)))
             del c
             torch.cuda.empty_cache()
         for nm in ("C2b", "C3"):
             log(f"extra: {nm} backward")
             c = Case(nm, dev, backward=True)
             c.fwd()
-            s_ = stats(time_launches(c.bwd, reps=5, warmup=1, flush=True))
+            s_ = stats(time_launches(c.bwd, reps=REPS, warmup=WARMUP, flush=True))
             tf = c.w.flops_bwd() / (s_["ms"] * 1e-3) / 1e12
             extra[nm + ".bwd"] = {"kernel": kernel_name(c.w, "bwd"), **s_, "tflops": round(tf, 2),
                                   "frac_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
@@ -793,8 +802,8 @@ def main():
             torch.cuda.empty_cache()
         log("extra: C4 forward + backward")
         c = Case("C4", dev, backward=True)
-        sf = stats(time_launches(c.fwd, reps=10, warmup=2, flush=True))
-        sb = stats(time_launches(c.bwd, reps=10, warmup=2, flush=True))
+        sf = stats(time_launches(c.fwd, reps=REPS, warmup=WARMUP, flush=True))
+        sb = stats(time_launches(c.bwd, reps=REPS, warmup=WARMUP, flush=True))
         extra["C4"] = {"fwd": {**sf, "tflops": round(c.w.flops_fwd() / (sf["ms"] * 1e-3) / 1e12, 2)},
                        "bwd": {**sb, "tflops": round(c.w.flops_bwd() / (sb["ms"] * 1e-3) / 1e12, 2)},
                        "fwd_bwd_tflops": round((c.w.flops_fwd() + c.w.flops_bwd())

@@ -280,7 +280,9 @@ def test_unsupported_raises():
 
 # ------------------------------------------------------------ full sizes ---
 
-FULL = ["C1", "C2a", "C2a_nc", "C2b", "C3", "C5"]
+# (with the two 50%-target shapes at the ends of the range: GQA at N = 8192 and
+# the longest, N = 32768, both on the looping grid with next-item copies)
+FULL = ["C1", "C2a", "C2a_nc", "C2b", "C3", "C5", "Ta_gqa", "Tc"]
 
 
 def _sampled_forward_check(wname, n_heads, n_rows):
