@@ -696,7 +696,9 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
     q.n_tiles = (p.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
     q.total = p.B * p.H_kv * q.n_tiles;
     q.group_items = q.n_tiles;                  // one (batch, K/V head) group per bh
-    q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
+    // (remap 3: each XCD takes its groups in turn, heaviest key tiles first)
+    q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0)
+                        : q.total % 8 != 0 ? 0 : (q.total / 8) % q.n_tiles == 0 ? 3 : 1;
     if (hipError_t e = launch_kernel(bwd_dkdv_kernel<D, CAUSAL, MASK>, dim3(q.total), dim3(DkdvCfg<D>::NT), s, q);
         e != hipSuccess)
       return e;
@@ -707,6 +709,12 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
     q.total = p.B * p.H * q.n_tiles;
     q.group_items = (p.H / p.H_kv) * q.n_tiles;
     q.remap = p.seqlens ? ((p.B * p.H_kv) % 8 == 0 ? 2 : 0) : (q.total % 8 == 0 ? 1 : 0);
+    if (q.remap == 1 && (q.total / 8) % q.group_items == 0) {
+      // whole (batch, K/V head) groups per XCD, their heads taken in turn
+      // (heaviest query tiles of every head first)
+      q.remap = 3;
+      q.group_items = q.n_tiles;
+    }
     return launch_kernel(bwd_dq_kernel<D, CAUSAL, MASK>, dim3(q.total), dim3(DqCfg<D>::NT), s, q);
   }
 }

@@ -186,6 +186,14 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 //   remap 1  each XCD takes a contiguous eighth of the items;
 //   remap 2  XCD x takes groups x, x + 8, x + 16, ... (for sequences of
 //            different lengths, so that every XCD gets a mix of them);
+//   remap 3  as remap 1, with the XCD's units of group_items consecutive
+//            items taken in turn (unit 0's first item, unit 1's first, ...,
+//            then every unit's second): the units' heaviest causal tiles
+//            all come first, so the dispatcher, which hands an XCD's
+//            workgroups to its CUs in order as they free up, pairs heavy
+//            with light (one unit after another left a CU that drew only
+//            heavy tiles at the end: the GQA prefill backward's dK/dV pass
+//            reached 68% of an even split in a dispatch model);
 //   remap 0  no map (the counts do not divide by 8).
 // Inside a head the heaviest causal tiles (largest q-tile index) come first.
 struct WorkItem {
@@ -197,6 +205,11 @@ __device__ __forceinline__ int xcd_item(int x, int s, int total, int group_items
   if (remap == 2) {
     const int gl = s / group_items, within = s - gl * group_items;
     return (x + 8 * gl) * group_items + within;
+  }
+  if (remap == 3) {
+    const int per = total >> 3, units = per / group_items;
+    const int k = s / units;
+    return x * per + (s - k * units) * group_items + k;
   }
   return x * (total >> 3) + s;
 }
