@@ -525,14 +525,20 @@ def counter_summary_rows(tables):
     return rows
 
 
+def _placeholder(run):
+    """'W=some/path/W_sq' -> 'W=<dir>/W_sq' (the summary names the run, not where it was written)."""
+    w, _, d = run.partition("=")
+    return f"{w}=<dir>/{os.path.basename(os.path.normpath(d))}"
+
+
 def write_counter_summary(rows, path, runs):
     f3 = lambda v, fmt: "—" if v is None else fmt.format(v)
     lines = ["# Matrix-pipe use, instruction mix and LDS waits per kernel (rocprofv3 counters)", "",
              "commands (from the repository root), one run per workload W and counter pass:", "",
-             "    rocprofv3 --kernel-trace --pmc " + " ".join(SQ_PASS) + " -d <dir>/W -o c --output-format csv -- "
+             "    rocprofv3 --kernel-trace --pmc " + " ".join(SQ_PASS) + " -d <dir>/W_sq -o c --output-format csv -- "
              "python3 bench.py --only W --steps 2 --warmup 0 --no-cpu-baseline --no-extra [--with-bwd]",
-             "    rocprofv3 --kernel-trace --pmc " + " ".join(LDS_PASS) + " (the same program, some W)",
-             "    python3 bench.py --counter-summary " + " ".join(runs) + " --summary-out <this file>", "",
+             "    rocprofv3 --kernel-trace --pmc " + " ".join(LDS_PASS) + " -d <dir>/W_lds (the same program, some W)",
+             "    python3 bench.py --counter-summary " + " ".join(_placeholder(r) for r in runs) + " --summary-out <this file>", "",
              "How the columns are formed: kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); "
              "clock = kernel cycles / duration (not shown under 20 us); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
              "1024 SIMDs / kernel cycles; co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / 1024 / kernel cycles; "
