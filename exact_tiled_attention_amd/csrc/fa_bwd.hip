@@ -681,6 +681,188 @@ void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// ========================================================== dQ, d = 256 ===
+// At d = 256 a wave that keeps Q, dO and dQ of 32 queries needs all 512
+// registers of a SIMD lane, so bwd_dq_kernel runs one wave a SIMD and nothing
+// hides its softmax work or its operand waits.  Here the two waves of a SIMD
+// share 32 queries and split the work by role: wave A (waves 0-3) keeps Q and
+// columns 0-127 of dQ, wave B (waves 4-7, on the same SIMDs) keeps dO and
+// columns 128-255.  Per 32-key block j, between two barriers: A forms S_j and
+// P_j = exp2(S_j c - LSE2) (masked) and hands P_j (fp32) over through LDS,
+// while B forms dP_j; then B forms dS_j = P_j (dP_j - D), hands it back and
+// adds its half of K_j^T dS_j, while A adds its half of K_{j-1}^T dS_{j-1}
+// (one block behind, so neither waits on the other inside a phase).  Both
+// halves see the same dS values in the same order as bwd_dq_kernel, so dQ
+// is the same bit for bit.  K/V tiles (64 keys, two blocks) are staged by
+// LDS DMA; the copy of stage s + 1 goes out at the second block of stage s,
+// when the block before it (still read by A) is done.  No masks other than
+// the causal one (padding, window and block-sparse calls keep bwd_dq_kernel).
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_pair_kernel(BwdParams p) {
+  constexpr int D = 256;
+  using C = DqCfg<D>;
+  constexpr int BR = C::BR, BC = C::BC, RB = C::RB, NW = 8, HD = D / 64;   // HD: 32-column blocks a half
+  constexpr int IPW = C::KTILE / 1024 / NW;   // 1 KB copies per wave and tensor
+  static_assert(BR == 4 * 32 && BC == 64, "four pairs of 32 queries, two 32-key blocks a stage");
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) float xp[4][16][64];                  // P_j, per pair
+  __shared__ __attribute__((aligned(1024))) unsigned long long xs[2][4][4][64];   // dS_j, dS_{j-1}
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2, pr = wid & 3;
+  const int lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const WorkItem wi = map_work(blockIdx.x, p.total, p.n_tiles, p.remap, p.group_items);
+  const int N = p.N;
+  const int b = wi.bh / p.H, h = wi.bh - b * p.H;
+  const int bkv = b * p.H_kv + h / (p.H / p.H_kv);
+  const int q_first = wi.qt * BR;
+  const int q0 = q_first + pr * 32;           // the pair's first query
+  const int myq = q0 + lr;
+  const unsigned char* kg = (const unsigned char*)p.k + (size_t)bkv * N * RB;
+  const unsigned char* vg = (const unsigned char*)p.v + (size_t)bkv * N * RB;
+
+  // A: Q rows (B operand of S^T = K Q^T); B: dO rows (of dP^T = V dO^T)
+  const bf16* src = (const bf16*)(grp == 0 ? p.q : p.dout) + (size_t)wi.bh * N * D;
+  bf16x8 qd[D / 16];
+#pragma unroll
+  for (int kb = 0; kb < D / 16; ++kb) {
+    bf16x8 x = {};
+    if (myq < N) x = *(const bf16x8*)(src + (size_t)myq * D + kb * 16 + 8 * g);
+    qd[kb] = x;
+  }
+  const float lse2 = myq < N ? p.lse2[(size_t)wi.bh * N + myq] : 0.f;
+  const float dlt = myq < N ? p.delta[(size_t)wi.bh * N + myq] : 0.f;
+  const float c = p.scale_log2;
+  f32x16 dq[HD];                              // A: columns 0-127, B: 128-255
+#pragma unroll
+  for (int i = 0; i < HD; ++i) dq[i] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(N, q_first + BR) : N;
+  const int n_st = (kv_end + BC - 1) / BC;   // stages (64-key tiles)
+  const int NB = 2 * n_st;                    // 32-key blocks
+  // a block some of whose keys precede some query of the pair
+  auto live = [&](int jb) { return jb >= 0 && jb < NB && !(CAUSAL && jb * 32 > q0 + 31); };
+
+  auto issue = [&](int t, unsigned char* st) {
+    const int key0 = t * BC;
+    const int bytes = min(N - key0, BC) * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)key0 * RB, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)key0 * RB, bytes);
+    const int dma0 = dma_base<RB, kSwzRt>(wid * IPW, __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      dma16_buf<0>(rk, dma_off<RB, kSwzRt>(dma0, i), st + (wid * IPW + i) * 1024);
+      dma16_buf<0>(rv, dma_off<RB, kSwzRt>(dma0, i), st + C::KTILE + (wid * IPW + i) * 1024);
+    }
+  };
+  auto stage_of = [&](int jb) -> unsigned char* { return ((jb >> 1) & 1) ? stage1 : stage0; };
+  auto offs = [&](int& rb0, int& tb0) {
+    const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    rb0 = (ln & 31) * RB + rt_swz<RB>(ln & 31, ln >> 5) * 16;
+    tb0 = tr_off<RB>(ln, 0, 0);
+    asm volatile("" : "+v"(rb0), "+v"(tb0));
+  };
+  // S^T (A: K rows) or dP^T (B: V rows) of block jb: lane = query, registers = keys
+  auto prod = [&](const unsigned char* rows) -> f32x16 {
+    int rb0, tb0;
+    offs(rb0, tb0);
+    f32x16 r = {};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+      const bf16x8 a = *(const bf16x8*)(rows + (rb0 ^ (rt_swz<RB>(0, 2 * kb) * 16)));
+      r = mfma_bf16(a, qd[kb], r);
+    }
+    return r;
+  };
+  // this wave's half of dQ^T += K^T dS^T for the block's K rows (transposing reads)
+  auto add_dq = [&](const unsigned char* krows, const unsigned long long* sw64) {
+    int rb0, tb0;
+    offs(rb0, tb0);
+    uint32_t sw[8];
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const unsigned long long x = sw64[j2 * 64 + lane];
+      sw[2 * j2] = (uint32_t)x;
+      sw[2 * j2 + 1] = (uint32_t)(x >> 32);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 ds = __builtin_bit_cast(bf16x8, i32x4{(int)sw[4 * half], (int)sw[4 * half + 1],
+                                                          (int)sw[4 * half + 2], (int)sw[4 * half + 3]});
+      const unsigned char* rb = krows + 16 * half * RB;
+#pragma unroll
+      for (int i = 0; i < HD; ++i) {
+        const int db = grp * HD + i;
+        const bf16x4 lo4 = lds_read_tr16(rb + (tb0 ^ (rt_swz<RB>(0, db * 4) * 16)));
+        const bf16x4 hi4 = lds_read_tr16(rb + (tb0 ^ (rt_swz<RB>(8, db * 4) * 16)) + 8 * RB);
+        dq[i] = mfma_bf16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), ds, dq[i]);
+      }
+    }
+  };
+
+  if (n_st > 0) issue(0, stage0);
+  if (grp == 0) {
+    // ---- A: S_j and P_j (to B); its half of K_{j-1}^T dS_{j-1} ----------------------
+    for (int jb = 0; jb <= NB; ++jb) {
+      if ((jb & 1) == 0) wait_vmem();
+      __syncthreads();
+      if ((jb & 1) == 1 && (jb >> 1) + 1 < n_st) issue((jb >> 1) + 1, stage_of(jb + 1));
+      if (live(jb)) {
+        const f32x16 s = prod(stage_of(jb) + (jb & 1) * 32 * RB);
+        const int key0 = jb * 32;
+        const bool masked = (key0 + 32 > N) || (CAUSAL && key0 + 31 > q0);
+        const int lim = min(CAUSAL ? myq : N - 1, N - 1) - key0 - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(fmaf(s[r], c, -lse2));
+          if (masked && (8 * (r >> 2) + (r & 3)) > lim) pv = 0.f;
+          xp[pr][r][lane] = pv;
+        }
+      }
+      __syncthreads();
+      if (live(jb - 1)) add_dq(stage_of(jb - 1) + ((jb - 1) & 1) * 32 * RB, &xs[(jb - 1) & 1][pr][0][0]);
+    }
+  } else {
+    // ---- B: dP_j; dS_j = P_j (dP_j - D) (to A) and its half of K_j^T dS_j ----------------
+    for (int jb = 0; jb <= NB; ++jb) {
+      if ((jb & 1) == 0) wait_vmem();
+      __syncthreads();
+      if ((jb & 1) == 1 && (jb >> 1) + 1 < n_st) issue((jb >> 1) + 1, stage_of(jb + 1));
+      f32x16 dp = {};
+      const bool lv = live(jb);
+      if (lv) dp = prod(stage_of(jb) + C::KTILE + (jb & 1) * 32 * RB);
+      __syncthreads();
+      if (lv) {
+        unsigned long long* dst = &xs[jb & 1][pr][0][0];
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const int r = 4 * j2;
+          const uint32_t lo = pack_bf16(xp[pr][r][lane] * (dp[r] - dlt), xp[pr][r + 1][lane] * (dp[r + 1] - dlt));
+          const uint32_t hi = pack_bf16(xp[pr][r + 2][lane] * (dp[r + 2] - dlt), xp[pr][r + 3][lane] * (dp[r + 3] - dlt));
+          dst[j2 * 64 + lane] = (unsigned long long)lo | ((unsigned long long)hi << 32);
+        }
+        add_dq(stage_of(jb) + (jb & 1) * 32 * RB, dst);
+      }
+    }
+  }
+
+  if (myq < N) {
+    bf16* dqr = (bf16*)p.dq + ((size_t)wi.bh * N + myq) * D + grp * (D / 2);
+    const float sc = p.scale;
+    const int g_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
+#pragma unroll
+    for (int i = 0; i < HD; ++i)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(i32x2*)(dqr + i * 32 + 8 * a + 4 * g_e) =
+            i32x2{(int)pack_bf16(dq[i][4 * a] * sc, dq[i][4 * a + 1] * sc),
+                  (int)pack_bf16(dq[i][4 * a + 2] * sc, dq[i][4 * a + 3] * sc)};
+  }
+}
+
 // ========================================================= launchers ======
 template <int D, bool CAUSAL, bool MASK>
 static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
@@ -714,6 +896,11 @@ static hipError_t launch_bwd(BwdParams p, hipStream_t s) {
       // (heaviest query tiles of every head first)
       q.remap = 3;
       q.group_items = q.n_tiles;
+    }
+    if constexpr (D == 256) {
+      // without padding, window or block masks: the paired-role kernel
+      if (p.seqlens == nullptr && p.window < 0 && p.block_mask == nullptr)
+        return launch_kernel(bwd_dq_pair_kernel<CAUSAL>, dim3(q.total), dim3(512), s, q);
     }
     return launch_kernel(bwd_dq_kernel<D, CAUSAL, MASK>, dim3(q.total), dim3(DqCfg<D>::NT), s, q);
   }
