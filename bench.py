@@ -282,7 +282,7 @@ def kernel_name(w, direction="fwd"):
 # instance table of fa_fwd.hip / fa_bwd.hip.
 LIB_KERNELS = ("fwd_bf16_kernel", "fwd_bf16_sp_kernel", "fwd_bf16_pp_kernel", "fwd_fp8_pp_kernel",
                "fwd_bf16_pairs_kernel", "fwd_f32_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel",
-               "bwd_dq_kernel", "kv_split_kernel", "kv_combine_kernel")
+               "bwd_dq_kernel", "bwd_dq_pair_kernel", "kv_split_kernel", "kv_combine_kernel")
 DOMINANT = {"C5": "fa::fwd_fp8_pp_kernel<128, true", "Ta": "fa::fwd_bf16_pp_kernel<128, true",
             "Ta_gqa": "fa::fwd_bf16_pp_kernel<128, true", "Tb": "fa::fwd_bf16_pp_kernel<128, true",
             "Tc": "fa::fwd_bf16_pp_kernel<128, true", "C3": "fa::fwd_bf16_pp_kernel<128, true",
