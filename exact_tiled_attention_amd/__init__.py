@@ -18,7 +18,7 @@ import os
 __all__ = ["fa_fwd", "fa_fwd_masked", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_masked",
            "fa_bwd_blocksparse", "fa_bwd_workspace_bytes", "fa_fwd_kvcache",
            "fa_fwd_kvcache_workspace_bytes", "fa_supported", "fa_kvcache_supported",
-           "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES"]
+           "fa_status_string", "FaError", "load_library", "LIB_PATH", "DTYPE_CODES", "attention"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -446,3 +446,45 @@ def fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = True, sca
                                   float(scale), int(bool(causal)), dt, _stream())
     _check(code)
     return dq, dk, dv
+
+
+# ------------------------------------------------------------ autograd ------
+# Training use (the pages' FlashAttention section on recomputing the L x L
+# matrix in the backward instead of storing it): the forward saves Q, K, V, O
+# and the per-row LSE only, and the backward hands them to fa_bwd, which
+# recomputes P tile by tile.  Both directions are the C entry points.
+_Attention = None
+
+
+def _attention_fn():
+    global _Attention
+    if _Attention is None:
+        torch = _torch()
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale):
+                o, lse = fa_fwd(q, k, v, causal=causal, scale=scale)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.causal, ctx.scale = causal, scale
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                # (autograd may hand a strided or expanded gradient; the C ABI
+                # takes dense [B][H][N][d] rows)
+                dq, dk, dv = fa_bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, scale=ctx.scale)
+                return dq, dk, dv, None, None
+
+    return _Attention
+
+
+def attention(q, k, v, causal: bool = True, scale: float | None = None):
+    """O = softmax(scale Q K^T [causal mask]) V with autograd support.
+
+    q [B, H, N, d], k and v [B, H_kv, N, d] (H a multiple of H_kv), bf16 for
+    the backward (fp32 and fp8 have forwards only).  The forward runs fa_fwd
+    and keeps its LSE; loss.backward() runs fa_bwd.  Gradients with respect to
+    k and v are per K/V head, summed over the query heads of each group."""
+    return _attention_fn().apply(q, k, v, bool(causal), scale)

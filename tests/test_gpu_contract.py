@@ -1,6 +1,7 @@
 """GPU checks of the library's contract beyond parity: bitwise repeatability
 of the backward, no device allocation at run time (no N x N buffer), fp8
-block scales of zero, and the binding's rejection of wrong tensors.
+block scales of zero, the binding's rejection of wrong tensors, and the
+autograd entry point.
 """
 import numpy as np
 import pytest
@@ -143,3 +144,24 @@ def test_binding_rejects_wrong_tensors():
     dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, do, workspace=ws)
     torch.cuda.synchronize()
     assert torch.isfinite(dq).all()
+
+
+@pytest.mark.parametrize("H,H_kv,causal", [(4, 2, True), (2, 2, False)])
+def test_attention_autograd_is_the_entry_points(H, H_kv, causal):
+    """fa.attention under autograd gives exactly fa_fwd's O and, for a strided
+    upstream gradient, exactly fa_bwd's dQ, dK, dV (per K/V head)."""
+    _say(f"autograd H={H}/{H_kv} causal={causal}")
+    w = syn.Workload("autograd", 2, H, H_kv, 333, 128, "bf16", causal, 1.0, 71, backward=True)
+    x = syn.make_inputs(w)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qa, ka, va, causal=causal)
+    do_strided = do.transpose(2, 3).contiguous().transpose(2, 3)
+    assert not do_strided.is_contiguous()
+    (o * do_strided).sum().backward()
+    o_ref, lse = fa.fa_fwd(q, k, v, causal=causal)
+    grads = fa.fa_bwd(q, k, v, o_ref, lse, do, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    for got, ref in zip((qa.grad, ka.grad, va.grad), grads):
+        assert got.shape == ref.shape and torch.equal(got, ref)
