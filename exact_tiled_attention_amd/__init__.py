@@ -461,12 +461,27 @@ def _attention_fn():
     if _Attention is None:
         torch = _torch()
 
+        def fwd(q, k, v, causal, scale, seqlens, window, block_mask):
+            if block_mask is not None:
+                return fa_fwd_blocksparse(q, k, v, block_mask, causal=causal, scale=scale)
+            if seqlens is not None or window is not None:
+                return fa_fwd_masked(q, k, v, seqlens=seqlens, window=window, causal=causal, scale=scale)
+            return fa_fwd(q, k, v, causal=causal, scale=scale)
+
+        def bwd(q, k, v, o, lse, do, causal, scale, seqlens, window, block_mask):
+            if block_mask is not None:
+                return fa_bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=causal, scale=scale)
+            if seqlens is not None or window is not None:
+                return fa_bwd_masked(q, k, v, o, lse, do, seqlens=seqlens, window=window, causal=causal,
+                                     scale=scale)
+            return fa_bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+
         class _Attention(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, causal, scale):
-                o, lse = fa_fwd(q, k, v, causal=causal, scale=scale)
+            def forward(ctx, q, k, v, causal, scale, seqlens, window, block_mask):
+                o, lse = fwd(q, k, v, causal, scale, seqlens, window, block_mask)
                 ctx.save_for_backward(q, k, v, o, lse)
-                ctx.causal, ctx.scale = causal, scale
+                ctx.args = (causal, scale, seqlens, window, block_mask)
                 return o
 
             @staticmethod
@@ -474,17 +489,24 @@ def _attention_fn():
                 q, k, v, o, lse = ctx.saved_tensors
                 # (autograd may hand a strided or expanded gradient; the C ABI
                 # takes dense [B][H][N][d] rows)
-                dq, dk, dv = fa_bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, scale=ctx.scale)
-                return dq, dk, dv, None, None
+                dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
+                return dq, dk, dv, None, None, None, None, None
 
     return _Attention
 
 
-def attention(q, k, v, causal: bool = True, scale: float | None = None):
-    """O = softmax(scale Q K^T [causal mask]) V with autograd support.
+def attention(q, k, v, causal: bool = True, scale: float | None = None, seqlens=None,
+              window: int | None = None, block_mask=None):
+    """O = softmax(scale Q K^T [masks]) V with autograd support.
 
     q [B, H, N, d], k and v [B, H_kv, N, d] (H a multiple of H_kv), bf16 for
-    the backward (fp32 and fp8 have forwards only).  The forward runs fa_fwd
-    and keeps its LSE; loss.backward() runs fa_bwd.  Gradients with respect to
-    k and v are per K/V head, summed over the query heads of each group."""
-    return _attention_fn().apply(q, k, v, bool(causal), scale)
+    the backward (fp32 and fp8 have forwards only).  Masks as in
+    fa_fwd_masked (seqlens: int32 [B] valid rows; window: query i sees keys
+    i - window .. i) or fa_fwd_blocksparse (block_mask: uint8 [H, nb, nb] of
+    128 x 128 blocks), not both.  The forward runs the matching fa_fwd* entry
+    point and keeps its LSE; loss.backward() runs the matching fa_bwd*.
+    Gradients with respect to k and v are per K/V head, summed over the query
+    heads of each group."""
+    if block_mask is not None and (seqlens is not None or window is not None):
+        raise ValueError("attention takes a block mask or seqlens/window, not both")
+    return _attention_fn().apply(q, k, v, bool(causal), scale, seqlens, window, block_mask)

@@ -165,3 +165,36 @@ def test_attention_autograd_is_the_entry_points(H, H_kv, causal):
     assert torch.equal(o.detach(), o_ref)
     for got, ref in zip((qa.grad, ka.grad, va.grad), grads):
         assert got.shape == ref.shape and torch.equal(got, ref)
+
+
+def test_attention_autograd_masks_are_the_entry_points():
+    """fa.attention with seqlens and a window, or with a block mask, gives
+    exactly the masked and block-sparse entry points' outputs and gradients."""
+    _say("autograd masked / block-sparse")
+    B, H, N, d = 2, 2, 384, 128
+    w = syn.Workload("autograd_m", B, H, H, N, d, "bf16", True, 1.0, 73, backward=True)
+    x = syn.make_inputs(w)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    seqlens = torch.tensor([300, 384], device=DEV, dtype=torch.int32)
+    nb = (N + 127) // 128
+    bm = (torch.rand(H, nb, nb, generator=torch.Generator().manual_seed(5)) < 0.6).to(torch.uint8)
+    bm[:, torch.arange(nb), torch.arange(nb)] = 1
+    bm = bm.to(DEV)
+    cases = [(dict(seqlens=seqlens, window=100),
+              lambda: fa.fa_fwd_masked(q, k, v, seqlens=seqlens, window=100, causal=True),
+              lambda o, lse: fa.fa_bwd_masked(q, k, v, o, lse, do, seqlens=seqlens, window=100, causal=True)),
+             (dict(block_mask=bm),
+              lambda: fa.fa_fwd_blocksparse(q, k, v, bm, causal=True),
+              lambda o, lse: fa.fa_bwd_blocksparse(q, k, v, o, lse, do, bm, causal=True))]
+    for kw, f_ref, b_ref in cases:
+        qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+        o = fa.attention(qa, ka, va, causal=True, **kw)
+        (o * do).sum().backward()
+        o_ref, lse = f_ref()
+        grads = b_ref(o_ref, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o.detach(), o_ref)
+        for got, ref in zip((qa.grad, ka.grad, va.grad), grads):
+            assert torch.equal(got, ref)
+    with pytest.raises(ValueError):
+        fa.attention(q, k, v, seqlens=seqlens, block_mask=bm)
